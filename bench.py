@@ -1,0 +1,378 @@
+#!/usr/bin/env python3
+"""Benchmark of the W2A8 ternary linear layer on one MI355X.
+
+Headline: the M = 1 GEMV (int8 activations x packed ternary weights -> bf16)
+at N = 13824, K = 2560 (the fused gate+up projection of the 2B-style model
+in the W2A8 page, "BitNet GPU 推理框架：从零构建 W2A8 的 2-bit 大模型 CUDA GEMV
+内核", §一 and §7.1), reported as microseconds per GEMV and achieved HBM
+GB/s against MI355X's 8 TB/s.
+
+Method:
+  * inputs are seeded synthetic data of the page's shapes (module ``synth``),
+    resident in HBM before timing starts;
+  * the packed weights are replicated into enough copies (>= 512 MiB in
+    total) that consecutive GEMVs never find their weights in the 256 MiB
+    Infinity Cache or the 4 MiB L2s; launch i reads copy i % copies;
+  * the K timed launches are captured in one HIP graph and replayed once,
+    bracketed by HIP events recorded on the stream the graph runs on, after
+    W untimed warm-up launches;
+  * bytes per GEMV = N*K/4 (packed weights) + M*K (int8 x) + 2*M*N (bf16 y)
+    + 4*M (s) + 2*ws_num (ws) -- the algorithmic bytes, each read once.
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published peak
+PEAK_INT8_TOPS = 5000.0          # MI355X dense int8 MFMA, published peak (TOP/s)
+A100_W2A8_GBS_13824x2560 = 473.5  # the page's 18.75 us on A100 (§7.1), as GB/s by the same formula
+CACHE_DEFEAT_BYTES = 512 << 20
+PROFILE_PMC = os.path.join(ROOT, "profiles", "gemv_i8_13824x2560_pmc.txt")
+GEMV_SOURCE = os.path.join(ROOT, "bit_gemv_bitlinear_amd", "csrc", "gemv.hip")
+
+
+def gemv_bytes(M, N, K, ws_num, x_bytes=1):
+    return N * K // 4 + x_bytes * M * K + 2 * M * N + 4 * M + 2 * ws_num
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def bf16_dev(bits):
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(
+        torch.bfloat16).cuda()
+
+
+def copies_for(nbytes):
+    return max(2, -(-CACHE_DEFEAT_BYTES // nbytes))
+
+
+def replicate(packed, n):
+    torch = _torch()
+    out = torch.empty((n, packed.numel()), dtype=torch.uint8, device=packed.device)
+    out.copy_(packed.unsqueeze(0).expand(n, -1))
+    return [out[i] for i in range(n)]
+
+
+def time_graph(launch, steps, warmup):
+    """Average ms per launch of `steps` launches captured in one graph (after `warmup` launches)."""
+    torch = _torch()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(min(warmup, 8)):
+            launch(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    if warmup > 8:
+        gw = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw):
+            for i in range(warmup - 8):
+                launch(i)
+        gw.replay()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            launch(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def headline(bl, steps, warmup):
+    """M=1 GEMV, N=13824, K=2560, ws_num=2, int8 uniform activations."""
+    torch = _torch()
+    c = synth.layer("gate_up")
+    packed = bl.pack_ternary_weights(torch.from_numpy(c.w).cuda())
+    n_copies = copies_for(packed.numel())
+    copies = replicate(packed, n_copies)
+    xq = torch.from_numpy(c.xq).cuda()
+    s = torch.from_numpy(c.s).cuda()
+    ws = bf16_dev(c.ws)
+    y = torch.empty((1, c.N), dtype=torch.bfloat16, device="cuda")
+    lib = bl.lib()
+    args = [xq.data_ptr(), None, s.data_ptr(), ws.data_ptr(), c.ws_num, y.data_ptr(), None, 1,
+            c.N, c.K]
+    ptrs = [p.data_ptr() for p in copies]
+
+    def launch(i):
+        args[1] = ptrs[i % n_copies]
+        rc = lib.bitlinear_i8xi2(*args, torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"bitlinear_i8xi2 failed: {rc}")
+
+    ms = time_graph(launch, steps, warmup)
+    return c, ms, n_copies
+
+
+def fused(bl, steps, warmup):
+    """Same shape, bf16 activations quantised per token inside the kernel."""
+    torch = _torch()
+    c = synth.make_float_gemv("gate_up_bf16", 1, 13824, 2560, 2, synth.seed_for(6), bf16=True)
+    packed = bl.pack_ternary_weights(torch.from_numpy(c.w).cuda())
+    n_copies = copies_for(packed.numel())
+    copies = replicate(packed, n_copies)
+    x = bf16_dev(c.x)
+    ws = bf16_dev(c.ws)
+    y = torch.empty((1, c.N), dtype=torch.bfloat16, device="cuda")
+    lib = bl.lib()
+    ptrs = [p.data_ptr() for p in copies]
+
+    def launch(i):
+        rc = lib.bitlinear_bf16_i8xi2(x.data_ptr(), ptrs[i % n_copies], ws.data_ptr(), c.ws_num,
+                                      y.data_ptr(), None, None, None, 1, c.N, c.K,
+                                      torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"bitlinear_bf16_i8xi2 failed: {rc}")
+
+    ms = time_graph(launch, steps, warmup)
+    return ms
+
+
+def layer_shapes(bl, steps, warmup):
+    torch = _torch()
+    out = {}
+    lib = bl.lib()
+    for c in synth.layer_set():
+        packed = bl.pack_ternary_weights(torch.from_numpy(c.w).cuda())
+        n_copies = copies_for(packed.numel())
+        copies = replicate(packed, n_copies)
+        ptrs = [p.data_ptr() for p in copies]
+        xq = torch.from_numpy(c.xq).cuda()
+        s = torch.from_numpy(c.s).cuda()
+        ws = bf16_dev(c.ws)
+        y = torch.empty((1, c.N), dtype=torch.bfloat16, device="cuda")
+
+        def launch(i, c=c, xq=xq, s=s, ws=ws, y=y, ptrs=ptrs, n_copies=n_copies):
+            rc = lib.bitlinear_i8xi2(xq.data_ptr(), ptrs[i % n_copies], s.data_ptr(),
+                                     ws.data_ptr(), c.ws_num, y.data_ptr(), None, 1, c.N, c.K,
+                                     torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"bitlinear_i8xi2 failed: {rc}")
+
+        ms = time_graph(launch, steps, warmup)
+        b = gemv_bytes(1, c.N, c.K, c.ws_num)
+        out[f"{c.name}_{c.N}x{c.K}"] = {"us": round(ms * 1e3, 3),
+                                        "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
+        del copies
+    return out
+
+
+def batched(bl, steps, warmup):
+    torch = _torch()
+    out = {}
+    lib = bl.lib()
+    for M in synth.BATCHED_M:
+        c = synth.batched(M)
+        packed = bl.pack_ternary_weights(torch.from_numpy(c.w).cuda())
+        n_copies = copies_for(packed.numel())
+        copies = replicate(packed, n_copies)
+        ptrs = [p.data_ptr() for p in copies]
+        q, s = bl.quantize_act_absmax_i8(torch.from_numpy(c.x).cuda())
+        ws = bf16_dev(c.ws)
+        y = torch.empty((M, c.N), dtype=torch.bfloat16, device="cuda")
+
+        def launch(i, c=c, q=q, s=s, ws=ws, y=y, ptrs=ptrs, n_copies=n_copies, M=M):
+            rc = lib.bitlinear_i8xi2(q.data_ptr(), ptrs[i % n_copies], s.data_ptr(), ws.data_ptr(),
+                                     c.ws_num, y.data_ptr(), None, M, c.N, c.K,
+                                     torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"bitlinear_i8xi2 failed: {rc}")
+
+        ms = time_graph(launch, steps, warmup)
+        b = gemv_bytes(M, c.N, c.K, c.ws_num)
+        ops = 2.0 * M * c.N * c.K
+        out[f"M{M}"] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                        "mfma_util": round(ops / (ms * 1e-3) / (PEAK_INT8_TOPS * 1e12), 4)}
+        del copies
+    return out
+
+
+def decode_step(bl, reps):
+    """30 layers x {qkv, o, gate+up, down}, fused quantisation, one bl_graph per step."""
+    torch = _torch()
+    calls = []
+    for c in synth.decode_step_nodes():
+        calls.append(dict(x=bf16_dev(c.x), packed=bl.pack_ternary_weights(torch.from_numpy(c.w).cuda()),
+                          ws=bf16_dev(c.ws), ws_num=c.ws_num,
+                          y=torch.empty((c.N,), dtype=torch.bfloat16, device="cuda"),
+                          N=c.N, K=c.K))
+    nbytes = sum(gemv_bytes(1, c["N"], c["K"], c["ws_num"], x_bytes=2) for c in calls)
+    g = bl.DecodeGraph(calls)
+    for _ in range(3):
+        g.launch()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.launch()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    g.close()
+    return {"us_per_step": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "bytes_per_step": nbytes, "gemvs_per_step": len(calls)}
+
+
+def torch_bf16_context(steps):
+    """The page's comparison column: torch bf16 matmul, 1 x 2560 by 2560 x 13824, weights rotated."""
+    torch = _torch()
+    g = torch.Generator(device="cuda").manual_seed(1)
+    n_copies = copies_for(13824 * 2560 * 2)
+    ws = [torch.randn((13824, 2560), device="cuda", dtype=torch.bfloat16, generator=g)
+          for _ in range(n_copies)]
+    x = torch.randn((1, 2560), device="cuda", dtype=torch.bfloat16, generator=g)
+    outs = torch.empty((1, 13824), device="cuda", dtype=torch.bfloat16)
+
+    def launch(i):
+        torch.matmul(x, ws[i % n_copies].t(), out=outs)
+
+    ms = time_graph(launch, steps, 16)
+    return {"us": round(ms * 1e3, 3)}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(seconds):
+    import oracle
+    c = synth.layer("gate_up")
+    oracle.bitlinear_i8(c.xq, c.w, c.s, c.ws, c.ws_num)     # load + warm
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.bitlinear_i8(c.xq, c.w, c.s, c.ws, c.ws_num)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    b = gemv_bytes(1, c.N, c.K, c.ws_num)
+    return {"value": round(b / per / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "us_per_gemv": round(per * 1e6, 1),
+            "sample": f"{n} full M=1 GEMVs at N=13824 K=2560 (int8 x, unpacked ternary w, int64 "
+                      f"sums, fp64 epilogue), single-threaded C, {el:.1f} s"}
+
+
+def pmc_traffic():
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it is for this kernel source."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    vals = {}
+    for line in open(PROFILE_PMC):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    src = hashlib.sha256(open(GEMV_SOURCE, "rb").read()).hexdigest()
+    if vals.get("gemv_source_sha256") != src or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--quick", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--pmc-calibrate", action="store_true",
+                    help="also run a plain copy of 256 MiB (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is not sharded across GPUs in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    torch = _torch()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import bit_gemv_bitlinear_amd as bl
+
+    c, ms, n_copies = headline(bl, args.steps, args.warmup)
+    nbytes = gemv_bytes(1, c.N, c.K, c.ws_num)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    detail = {}
+    if args.pmc_calibrate:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        detail["calibration_copy_bytes"] = 256 << 20
+    if not args.quick:
+        detail["fused_bf16_13824x2560"] = {}
+        fms = fused(bl, max(args.steps // 2, 100), min(args.warmup, 100))
+        fb = gemv_bytes(1, 13824, 2560, 2, x_bytes=2)
+        detail["fused_bf16_13824x2560"] = {"us": round(fms * 1e3, 3),
+                                           "GBps": round(fb / (fms * 1e-3) / 1e9, 1)}
+        detail["layer_set_int8"] = layer_shapes(bl, max(args.steps // 4, 100), 50)
+        detail["batched_mfma"] = batched(bl, max(args.steps // 8, 50), 20)
+        detail["decode_step_graph"] = decode_step(bl, 20)
+        detail["torch_bf16_matmul_13824x2560"] = torch_bf16_context(200)
+
+    traffic = pmc_traffic()
+    line = {
+        "metric": "M=1 W2A8 GEMV µs + achieved HBM GB/s (% of peak) at N=13824,K=2560",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "us_per_gemv": round(ms * 1e3, 3),
+        "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(gbs / A100_W2A8_GBS_13824x2560, 3),
+        "vs_baseline_note": "context only: the page's A100 kernel, host-timed 18.75 us = 473.5 GB/s",
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "M=1 W2A8 GEMV N=13824 K=2560 (gate+up of a 2B-style layer), "
+                               "uniform ternary weights, uniform int8 activations, ws_num=2",
+                   "M": 1, "N": c.N, "K": c.K, "ws_num": c.ws_num,
+                   "bytes_per_gemv": nbytes, "weight_copies": n_copies,
+                   "timing": "one HIP graph of `steps` launches, HIP events on its stream"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic},
+    }
+    if detail:
+        line["detail"] = detail
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+"""Python binding of libbitlinear.so, the gfx950 W2A8 ternary linear layer.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI of include/bitlinear.h.  torch provides device memory and
+streams; the functions take and return torch tensors on the current HIP
+device and enqueue on ``torch.cuda.current_stream()``.
+
+The library is loaded on first use; if it has not been built, or a call is
+made without a GPU, the call raises -- there is no fallback of any kind.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP, BL_ERR_ARG = 0, -1, -2, -3, -4, -5
+
+# Entry points declared in include/bitlinear.h: name -> (restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+SIGNATURES = {
+    "bl_status_string": (ctypes.c_char_p, [_I]),
+    "bl_abi_version": (_I, []),
+    "bl_packed_bytes": (ctypes.c_size_t, [_I, _I]),
+    "pack_ternary_weights": (_I, [_P, _P, _I, _I, _P, _P]),
+    "bl_pack_ternary_host": (ctypes.c_int64, [_P, _P, _I, _I]),
+    "quantize_act_absmax_i8": (_I, [_P, _I, _P, _P, _I, _I, _P]),
+    "bitlinear_i8xi2": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _P]),
+    "bitlinear_bf16_i8xi2": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "bl_graph_create": (_I, [_P, _I, ctypes.POINTER(_P)]),
+    "bl_graph_launch": (_I, [_P, _P]),
+    "bl_graph_size": (_I, [_P]),
+    "bl_graph_destroy": (_I, [_P]),
+}
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class bl_gemv_desc(ctypes.Structure):
+    _fields_ = [("x", _P), ("packed", _P), ("ws", _P), ("ws_num", _I), ("y", _P), ("acc", _P),
+                ("N", _I), ("K", _I)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (ctypes.CDLL), with argument types set."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run bit_gemv_bitlinear_amd/build.py "
+                              "(or __graft_entry__.build())")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().bl_status_string(status).decode()
+
+
+def _check(status, what):
+    if status != BL_OK:
+        raise BitLinearError(status, what)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, dtype, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def bl_packed_bytes(N: int, K: int) -> int:
+    return int(lib().bl_packed_bytes(N, K))
+
+
+def pack_ternary_weights(w, n_invalid=None):
+    """Pack an int8 N x K ternary matrix (device) into the 64x64-tile layout (uint8 tensor)."""
+    import torch
+    _require(w, torch.int8, "w")
+    N, K = w.shape
+    packed = torch.empty(bl_packed_bytes(N, K), dtype=torch.uint8, device=w.device)
+    if n_invalid is not None:
+        _require(n_invalid, torch.int32, "n_invalid")
+    _check(lib().pack_ternary_weights(_ptr(w), _ptr(packed), N, K, _ptr(n_invalid), _stream()),
+           "pack_ternary_weights")
+    return packed
+
+
+def bl_pack_ternary_host(w: np.ndarray):
+    """Host twin of pack_ternary_weights on a numpy int8 N x K array -> (packed uint8, n_invalid)."""
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    N, K = w.shape
+    out = np.zeros(bl_packed_bytes(N, K), dtype=np.uint8)
+    r = lib().bl_pack_ternary_host(w.ctypes.data_as(_P), out.ctypes.data_as(_P), N, K)
+    if r < 0:
+        raise BitLinearError(int(r), "bl_pack_ternary_host")
+    return out, int(r)
+
+
+def quantize_act_absmax_i8(x):
+    """Per-row absmax int8 quantisation of fp32 or bf16 M x K (device) -> (q int8, s fp32)."""
+    import torch
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    _require(x, x.dtype, "x")
+    x2 = x.reshape(-1, x.shape[-1])
+    M, K = x2.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    s = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().quantize_act_absmax_i8(_ptr(x2), 1 if x.dtype == torch.bfloat16 else 0, _ptr(q),
+                                        _ptr(s), M, K, _stream()), "quantize_act_absmax_i8")
+    return q, s
+
+
+def bitlinear_i8xi2(xq, packed, s, ws, N, ws_num=None, y=None, acc=None):
+    """int8 activations (M x K), packed weights, fp32 s (M), bf16 ws -> bf16 y (M x N).
+
+    ``acc`` (int32 M x N) receives the int32 accumulators when given; ``y``
+    may be passed to reuse an output buffer.
+    """
+    import torch
+    _require(xq, torch.int8, "xq")
+    _require(packed, torch.uint8, "packed")
+    _require(s, torch.float32, "s")
+    _require(ws, torch.bfloat16, "ws")
+    xq2 = xq.reshape(-1, xq.shape[-1])
+    M, K = xq2.shape
+    ws_num = ws.numel() if ws_num is None else ws_num
+    if packed.numel() != bl_packed_bytes(N, K):
+        raise ValueError("packed has the wrong size for (N, K)")
+    if s.numel() != M:
+        raise ValueError("s must have one scale per row")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _require(y, torch.bfloat16, "y")
+    if acc is not None:
+        _require(acc, torch.int32, "acc")
+    _check(lib().bitlinear_i8xi2(_ptr(xq2), _ptr(packed), _ptr(s), _ptr(ws), ws_num, _ptr(y),
+                                 _ptr(acc), M, N, K, _stream()), "bitlinear_i8xi2")
+    return y
+
+
+def bitlinear_bf16_i8xi2(x, packed, ws, N, ws_num=None, y=None, q_out=None, s_out=None, acc=None):
+    """bf16 activations (M x K) -> per-token int8 quantisation + the layer -> bf16 y (M x N).
+
+    For M > 1 the quantised activations are staged in ``q_out``/``s_out``;
+    they are allocated here when not given.
+    """
+    import torch
+    _require(x, torch.bfloat16, "x")
+    _require(packed, torch.uint8, "packed")
+    _require(ws, torch.bfloat16, "ws")
+    x2 = x.reshape(-1, x.shape[-1])
+    M, K = x2.shape
+    ws_num = ws.numel() if ws_num is None else ws_num
+    if packed.numel() != bl_packed_bytes(N, K):
+        raise ValueError("packed has the wrong size for (N, K)")
+    if (M > 1 or K > 65536) and q_out is None:
+        q_out = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if (M > 1 or K > 65536) and s_out is None:
+        s_out = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib().bitlinear_bf16_i8xi2(_ptr(x2), _ptr(packed), _ptr(ws), ws_num, _ptr(y),
+                                      _ptr(q_out), _ptr(s_out), _ptr(acc), M, N, K, _stream()),
+           "bitlinear_bf16_i8xi2")
+    return y
+
+
+class DecodeGraph:
+    """A chain of M = 1 bf16 layer calls captured once (bl_graph_create) and replayed.
+
+    ``calls`` is a list of dicts with keys x, packed, ws, ws_num, y, N, K and
+    optionally acc (device tensors); they must stay alive as long as the graph.
+    """
+
+    def __init__(self, calls):
+        self._keep = calls
+        arr = (bl_gemv_desc * len(calls))()
+        for i, c in enumerate(calls):
+            arr[i] = bl_gemv_desc(c["x"].data_ptr(), c["packed"].data_ptr(), c["ws"].data_ptr(),
+                                  c["ws_num"], c["y"].data_ptr(),
+                                  c["acc"].data_ptr() if c.get("acc") is not None else None,
+                                  c["N"], c["K"])
+        h = ctypes.c_void_p()
+        _check(lib().bl_graph_create(arr, len(calls), ctypes.byref(h)), "bl_graph_create")
+        self._h = h
+
+    def __len__(self):
+        return lib().bl_graph_size(self._h)
+
+    def launch(self):
+        _check(lib().bl_graph_launch(self._h, _stream()), "bl_graph_launch")
+
+    def close(self):
+        if self._h:
+            _check(lib().bl_graph_destroy(self._h), "bl_graph_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

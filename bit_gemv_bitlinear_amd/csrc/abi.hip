@@ -1,0 +1,213 @@
+// abi.hip -- the C ABI declared in include/bitlinear.h: host-side argument
+// checks, kernel selection, and the decode-step graph.
+//
+// Source page: "BitNet GPU 推理框架：从零构建 W2A8 的 2-bit 大模型 CUDA GEMV 内核"
+// (blog.gitcode.com), cited as [W2A8]: §二 2.2 (one exported C entry taking
+// int8 activations, packed weights, bf16 output, scales, M, N, K and a
+// stream), §六 item 1 (each decode step replayed as a captured graph).  The
+// page's library selects a kernel by exact (M, N, K) and prints when none
+// matches; this one accepts any shape in range and returns a status code.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "bitlinear.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxK = 1 << 20;
+constexpr int kMaxN = 1 << 24;
+constexpr int kMaxWsNum = 64;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_mnk(int M, int N, int K) {
+    if (M < 1 || N < 1 || K < 16 || (K % 16) != 0 || K > kMaxK || N > kMaxN) return BL_ERR_SHAPE;
+    // the largest output buffer indexed with size_t; M * N bounded for int grids
+    if (static_cast<long long>(M) * N > (1LL << 40)) return BL_ERR_SHAPE;
+    return BL_OK;
+}
+
+int check_ws(int ws_num, int N) {
+    if (ws_num < 1 || ws_num > kMaxWsNum || (N % ws_num) != 0) return BL_ERR_ARG;
+    return BL_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+int check_layer_i8(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,
+                   int ws_num, const uint16_t* y, const int32_t* acc, int M, int N, int K) {
+    if (!xq || !packed || !s || !ws || !y) return BL_ERR_NULL;
+    int rc = check_mnk(M, N, K);
+    if (rc) return rc;
+    if ((rc = check_ws(ws_num, N))) return rc;
+    if (!aligned(xq, 16) || !aligned(packed, 16) || !aligned(s, 4) || !aligned(ws, 2) ||
+        !aligned(y, 2) || (acc && !aligned(acc, 4)))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+int check_layer_bf16(const uint16_t* x, const uint8_t* packed, const uint16_t* ws, int ws_num,
+                     const uint16_t* y, const int8_t* q_out, const float* s_out,
+                     const int32_t* acc, int M, int N, int K) {
+    if (!x || !packed || !ws || !y) return BL_ERR_NULL;
+    int rc = check_mnk(M, N, K);
+    if (rc) return rc;
+    if ((rc = check_ws(ws_num, N))) return rc;
+    const bool staged = (M > 1) || (K > bl::kFusedMaxK);
+    if (staged && (!q_out || !s_out)) return BL_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(ws, 2) || !aligned(y, 2) ||
+        (q_out && !aligned(q_out, 16)) || (s_out && !aligned(s_out, 4)) ||
+        (acc && !aligned(acc, 4)))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+int run_layer_i8(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,
+                 int ws_num, uint16_t* y, int32_t* acc, int M, int N, int K, hipStream_t stream) {
+    if (M == 1)
+        return status_of(bl::launch_gemv_i8(xq, packed, s, ws, ws_num, y, acc, N, K, stream));
+    return status_of(bl::launch_gemm_mfma(xq, packed, s, ws, ws_num, y, acc, M, N, K, stream));
+}
+
+int run_layer_bf16(const uint16_t* x, const uint8_t* packed, const uint16_t* ws, int ws_num,
+                   uint16_t* y, int8_t* q_out, float* s_out, int32_t* acc, int M, int N, int K,
+                   hipStream_t stream) {
+    if (M == 1 && K <= bl::kFusedMaxK)
+        return status_of(bl::launch_gemv_bf16_fused(x, packed, ws, ws_num, y, q_out, s_out, acc,
+                                                    N, K, stream));
+    int rc = status_of(bl::launch_quant(x, 1, q_out, s_out, M, K, stream));
+    if (rc) return rc;
+    return run_layer_i8(q_out, packed, s_out, ws, ws_num, y, acc, M, N, K, stream);
+}
+
+}  // namespace
+
+struct bl_graph {
+    hipGraphExec_t exec;
+    int n;
+};
+
+extern "C" {
+
+const char* bl_status_string(int status) {
+    switch (status) {
+        case BL_OK: return "ok";
+        case BL_ERR_NULL: return "a required pointer is NULL";
+        case BL_ERR_SHAPE: return "M, N or K outside the supported range";
+        case BL_ERR_ALIGN: return "a pointer is not aligned as required";
+        case BL_ERR_HIP: return "the HIP runtime reported an error";
+        case BL_ERR_ARG: return "bad argument";
+        default: return "unknown status";
+    }
+}
+
+int bl_abi_version(void) { return 1; }
+
+size_t bl_packed_bytes(int N, int K) { return bl::packed_bytes(N, K); }
+
+int pack_ternary_weights(const int8_t* w, uint8_t* packed, int N, int K, int32_t* n_invalid,
+                         hipStream_t stream) {
+    if (!w || !packed) return BL_ERR_NULL;
+    if (N < 1 || K < 1 || N > kMaxN || K > kMaxK) return BL_ERR_SHAPE;
+    if (!aligned(packed, 16) || (n_invalid && !aligned(n_invalid, 4))) return BL_ERR_ALIGN;
+    (void)hipGetLastError();
+    return status_of(bl::launch_pack(w, packed, N, K, n_invalid, stream));
+}
+
+int64_t bl_pack_ternary_host(const int8_t* w_host, uint8_t* packed_host, int N, int K) {
+    if (!w_host || !packed_host) return BL_ERR_NULL;
+    if (N < 1 || K < 1 || N > kMaxN || K > kMaxK) return BL_ERR_SHAPE;
+    if (!aligned(packed_host, 4)) return BL_ERR_ALIGN;
+    return bl::pack_host(w_host, packed_host, N, K);
+}
+
+int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int M, int K,
+                           hipStream_t stream) {
+    if (!x || !q || !s) return BL_ERR_NULL;
+    if (x_dtype != 0 && x_dtype != 1) return BL_ERR_ARG;
+    if (M < 1 || K < 16 || (K % 16) != 0 || K > kMaxK) return BL_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return BL_ERR_ALIGN;
+    (void)hipGetLastError();
+    return status_of(bl::launch_quant(x, x_dtype, q, s, M, K, stream));
+}
+
+int bitlinear_i8xi2(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,
+                    int ws_num, uint16_t* y, int32_t* acc, int M, int N, int K,
+                    hipStream_t stream) {
+    const int rc = check_layer_i8(xq, packed, s, ws, ws_num, y, acc, M, N, K);
+    if (rc) return rc;
+    (void)hipGetLastError();
+    return run_layer_i8(xq, packed, s, ws, ws_num, y, acc, M, N, K, stream);
+}
+
+int bitlinear_bf16_i8xi2(const uint16_t* x, const uint8_t* packed, const uint16_t* ws,
+                         int ws_num, uint16_t* y, int8_t* q_out, float* s_out, int32_t* acc,
+                         int M, int N, int K, hipStream_t stream) {
+    const int rc = check_layer_bf16(x, packed, ws, ws_num, y, q_out, s_out, acc, M, N, K);
+    if (rc) return rc;
+    (void)hipGetLastError();
+    return run_layer_bf16(x, packed, ws, ws_num, y, q_out, s_out, acc, M, N, K, stream);
+}
+
+int bl_graph_create(const bl_gemv_desc* descs, int n, bl_graph** out) {
+    if (!out) return BL_ERR_NULL;
+    *out = nullptr;
+    if (!descs) return BL_ERR_NULL;
+    if (n < 1 || n > 65536) return BL_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        const bl_gemv_desc& d = descs[i];
+        const int rc = check_layer_bf16(d.x, d.packed, d.ws, d.ws_num, d.y, nullptr, nullptr,
+                                        d.acc, 1, d.N, d.K);
+        if (rc) return rc;
+    }
+    (void)hipGetLastError();
+    hipStream_t cs = nullptr;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return BL_ERR_HIP;
+    int rc = BL_OK;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        rc = BL_ERR_HIP;
+    } else {
+        for (int i = 0; i < n && rc == BL_OK; ++i) {
+            const bl_gemv_desc& d = descs[i];
+            rc = run_layer_bf16(d.x, d.packed, d.ws, d.ws_num, d.y, nullptr, nullptr, d.acc, 1,
+                                d.N, d.K, cs);
+        }
+        const hipError_t e = hipStreamEndCapture(cs, &graph);
+        if (rc == BL_OK && e != hipSuccess) rc = BL_ERR_HIP;
+    }
+    if (rc == BL_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess)
+        rc = BL_ERR_HIP;
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(cs);
+    if (rc != BL_OK) {
+        if (exec) (void)hipGraphExecDestroy(exec);
+        return rc;
+    }
+    bl_graph* g = new (std::nothrow) bl_graph{exec, n};
+    if (!g) {
+        (void)hipGraphExecDestroy(exec);
+        return BL_ERR_ARG;
+    }
+    *out = g;
+    return BL_OK;
+}
+
+int bl_graph_launch(bl_graph* graph, hipStream_t stream) {
+    if (!graph) return BL_ERR_NULL;
+    return status_of(hipGraphLaunch(graph->exec, stream));
+}
+
+int bl_graph_size(const bl_graph* graph) { return graph ? graph->n : BL_ERR_NULL; }
+
+int bl_graph_destroy(bl_graph* graph) {
+    if (!graph) return BL_OK;
+    const hipError_t e = hipGraphExecDestroy(graph->exec);
+    delete graph;
+    return status_of(e);
+}
+
+}  // extern "C"

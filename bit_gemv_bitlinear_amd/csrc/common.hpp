@@ -1,0 +1,95 @@
+// common.hpp -- device-side helpers shared by the gfx950 kernels of the W2A8
+// ternary linear layer.  Source page: "BitNet GPU 推理框架：从零构建 W2A8 的
+// 2-bit 大模型 CUDA GEMV 内核" (blog.gitcode.com), cited as [W2A8].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+// Geometry of the packed layout: a tile is 64 rows x 64 K = 1024 bytes; row
+// slot r of a tile is 16 bytes = four 32-bit words of 16 consecutive K.
+constexpr int kTileRows = 64;
+constexpr int kTileK = 64;
+constexpr int kTileBytes = 1024;
+
+// Table for v_perm_b32: byte c of this word is the int8 weight of 2-bit code
+// c.  Code 1 -> -1 (0xFF), 2 -> 0, 3 -> +1; code 0 (padding) -> 0.
+constexpr uint32_t kCodeToInt8 = 0x0100FF00u;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round an fp64 value to bf16, ties to even, straight from the fp64 bits (no
+// intermediate fp32 rounding, so there is no double rounding).  A bf16 value
+// is r * 2^q with q = E - 7 for |v| >= 2^-126 (E = exponent of the leading
+// bit) and q = -133 below; its encoding is ((q + 133) << 7) + r, which also
+// carries correctly into the exponent when rounding reaches the next binade.
+__device__ __forceinline__ uint16_t bf16_from_double_rne(double v) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t sign = static_cast<uint32_t>(b >> 48) & 0x8000u;
+    const uint64_t mag = b & 0x7FFFFFFFFFFFFFFFull;
+    if (mag > 0x7FF0000000000000ull) return static_cast<uint16_t>(sign | 0x7FC0u);   // NaN
+    if (mag >= 0x7FF0000000000000ull) return static_cast<uint16_t>(sign | 0x7F80u);  // inf
+    const int exp = static_cast<int>(mag >> 52);
+    if (exp == 0) return static_cast<uint16_t>(sign);   // |v| < 2^-1022 rounds to zero
+    const int E = exp - 1023;
+    const uint64_t m = (mag & ((1ull << 52) - 1)) | (1ull << 52);   // v = m * 2^(E-52)
+    const int q = (E >= -126) ? (E - 7) : -133;
+    const int shift = q - (E - 52);                                  // >= 45
+    if (shift > 54) return static_cast<uint16_t>(sign);             // below half of 2^-133
+    uint64_t r = m >> shift;
+    const uint64_t rem = m & ((1ull << shift) - 1);
+    const uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (r & 1))) ++r;
+    int64_t bits = (static_cast<int64_t>(q + 133) << 7) + static_cast<int64_t>(r);
+    if (bits >= 0x7F80) bits = 0x7F80;
+    return static_cast<uint16_t>(sign | static_cast<uint32_t>(bits));
+}
+
+// The epilogue of [W2A8] §5.3 under the reading y = acc * ws / s: the
+// activation scale s = 127/amax multiplied x on the way in, so it divides
+// here.  Evaluated in fp64 ((acc * ws) is exact; one rounding for the
+// quotient) and rounded once to bf16.
+__device__ __forceinline__ uint16_t epilogue_bf16(int32_t acc, float ws, float s) {
+    const double v = (static_cast<double>(acc) * static_cast<double>(ws)) / static_cast<double>(s);
+    return bf16_from_double_rne(v);
+}
+
+// Per-activation quantisation of [W2A8] §六 item 3: round half to even of
+// x * s in fp32 (v_rndne_f32), clamped to [-128, 127].
+__device__ __forceinline__ int quant_one(float x, float s) {
+    float r = __builtin_rintf(x * s);
+    r = fminf(fmaxf(r, -128.0f), 127.0f);
+    return static_cast<int>(r);
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+    return (static_cast<uint32_t>(a) & 0xFFu) | ((static_cast<uint32_t>(b) & 0xFFu) << 8) |
+           ((static_cast<uint32_t>(c) & 0xFFu) << 16) | ((static_cast<uint32_t>(d) & 0xFFu) << 24);
+}
+
+// Signed int8x4 dot product with int32 accumulate, no saturation (v_dot4_i32_i8).
+__device__ __forceinline__ int dot4(int a, int b, int c) {
+    return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// Wave-wide reductions over the 64 lanes.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace bl

@@ -1,0 +1,37 @@
+// kernels.hpp -- internal host-side launchers of the gfx950 kernels.  The
+// launchers assume validated arguments (the C ABI in abi.hip validates) and
+// return the status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bl {
+
+size_t packed_bytes(int N, int K);
+
+hipError_t launch_pack(const int8_t* w, uint8_t* packed, int N, int K, int32_t* n_invalid,
+                       hipStream_t stream);
+int64_t pack_host(const int8_t* w, uint8_t* packed, int N, int K);
+
+hipError_t launch_quant(const void* x, int x_is_bf16, int8_t* q, float* s, int M, int K,
+                        hipStream_t stream);
+
+// M == 1, int8 activations.
+hipError_t launch_gemv_i8(const int8_t* xq, const uint8_t* packed, const float* s,
+                          const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int N, int K,
+                          hipStream_t stream);
+
+// M == 1, bf16 activations quantised inside the kernel; K <= kFusedMaxK.
+constexpr int kFusedMaxK = 65536;
+hipError_t launch_gemv_bf16_fused(const uint16_t* x, const uint8_t* packed, const uint16_t* ws,
+                                  int ws_num, uint16_t* y, int8_t* q_out, float* s_out,
+                                  int32_t* acc, int N, int K, hipStream_t stream);
+
+// M >= 2, int8 activations, int8 MFMA.
+hipError_t launch_gemm_mfma(const int8_t* xq, const uint8_t* packed, const float* s,
+                            const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int M,
+                            int N, int K, hipStream_t stream);
+
+}  // namespace bl

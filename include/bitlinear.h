@@ -1,0 +1,209 @@
+/*
+ * bitlinear.h -- C ABI of the BitNet b1.58 W2A8 ternary linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer: ternary weights {-1, 0, +1} packed four to a byte, per-token
+ * absmax int8 activations, exact int32 dot products, rescaled by the weight
+ * and activation scales to bf16.  Source page: "BitNet GPU 推理框架：从零构建
+ * W2A8 的 2-bit 大模型 CUDA GEMV 内核" (blog.gitcode.com), cited as [W2A8]:
+ *   §二 2.2   the single exported entry of the page's library (int8
+ *             activations, packed weights, bf16 output, activation scale,
+ *             weight scales, M, N, K, stream);
+ *   §四 4.2   ternary weights and one bf16 scale per matrix (or per fused
+ *             sub-matrix);
+ *   §5.1-5.3  packing, decoding, int8 dot products, the epilogue
+ *             out = acc * scales, with weight scale ws[n / (N / ws_num)];
+ *   §六 item 3 per-token activation quantisation s = 127 / max|x|, round,
+ *             clamp to [-128, 127];
+ *   §六 item 1 the decode step captured as a graph and replayed.
+ *
+ * Conventions shared by every call
+ *   - Pointers are device pointers unless the name ends in _host.
+ *   - bf16 values travel as uint16_t bit patterns.
+ *   - Every call checks its arguments on the host first and returns a
+ *     negative BL_ERR_* code without touching the device if one is wrong;
+ *     otherwise it enqueues work on `stream` and returns BL_OK without
+ *     synchronising.  A launch failure reported by the runtime returns
+ *     BL_ERR_HIP.  Nothing is printed.
+ *   - The caller owns every buffer and keeps it alive until the work on
+ *     `stream` (or the graph that captured it) has completed.
+ *   - No call allocates or frees device memory except bl_graph_create /
+ *     bl_graph_destroy (graph objects) and the library holds no global
+ *     state, so calls on different streams may run concurrently when their
+ *     outputs do not overlap.
+ *   - Alignment: xq, x, packed and q_out 16 bytes; s, s_out, acc 4 bytes;
+ *     ws, y 2 bytes.  Otherwise BL_ERR_ALIGN.
+ *   - Shapes: M >= 1, N >= 1, K >= 16 with K % 16 == 0, K <= 1048576,
+ *     N <= 16777216.  Otherwise BL_ERR_SHAPE.
+ *   - Activation inputs must be finite; scales must be finite and > 0.
+ *     These are not checked on the device; other values give undefined
+ *     results (never out-of-bounds accesses).
+ *
+ * Packed weight layout ("64x64 tiles")
+ *   The weight w[n][k] of an N x K matrix (row n produces output n) is the
+ *   2-bit code w + 2 ({-1,0,1} -> {1,2,3}, [W2A8] §5.2).  Code 0 marks
+ *   padding.  With S = ceil(K/64) steps and ceil(N/64) bands:
+ *     tile  t = (n / 64) * S + k / 64          1024 bytes per tile
+ *     byte  t*1024 + 16*(n % 64) + 4*((k % 64) / 16) + (k % 16) % 4
+ *     bits  2*((k % 16) / 4) and the next one
+ *   i.e. a tile is 64 rows x 64 K; row slot r holds 16 bytes = four 32-bit
+ *   words of 16 consecutive K each, and inside a word element e sits at bit
+ *   8*(e%4) + 2*(e/4): the page's interleave 0,4,8,12,1,5,... ([W2A8] §5.2),
+ *   so (word >> 2i) & 0x03030303 holds elements 4i..4i+3 as bytes.  Lane r of
+ *   a 64-wide wavefront reads row slot r with one 16-byte load, and a
+ *   wavefront's load of a tile is 1 KiB contiguous.  Rows n >= N and columns
+ *   k >= K of the last tiles are code 0.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define BL_OK 0
+#define BL_ERR_NULL (-1)   /* a required pointer is NULL */
+#define BL_ERR_SHAPE (-2)  /* M, N, K outside the supported range */
+#define BL_ERR_ALIGN (-3)  /* a pointer is not aligned as required */
+#define BL_ERR_HIP (-4)    /* the HIP runtime reported an error */
+#define BL_ERR_ARG (-5)    /* any other bad argument (ws_num, dtype, n) */
+
+/* Static description of a status code (never NULL). */
+const char* bl_status_string(int status);
+
+/* Version of this ABI; bumped on any incompatible change. */
+int bl_abi_version(void);
+
+/*
+ * Size in bytes of the packed buffer for an N x K matrix:
+ * ceil(N/64) * ceil(K/64) * 1024 (exactly N*K/4 when 64 divides N and K).
+ * Returns 0 for N < 1 or K < 1.
+ */
+size_t bl_packed_bytes(int N, int K);
+
+/*
+ * pack_ternary_weights -- pack a ternary matrix into the 64x64-tile layout
+ * ([W2A8] §5.1-5.2: code w + 2, four codes per byte, interleaved words).
+ *   w          device, int8, N x K row-major (row n = output n)
+ *   packed     device, bl_packed_bytes(N, K) bytes, written in full
+ *              (padding included)
+ *   n_invalid  device int32 counter or NULL; when given, the number of
+ *              entries of w outside {-1, 0, 1} is ADDED to it (those entries
+ *              are packed as code 0, which the layer reads as weight -2 for
+ *              M = 1 and 0 for M > 1: an invalid matrix gives undefined
+ *              results)
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (K % 16 != 0 is allowed here: any
+ * N, K >= 1), BL_ERR_ALIGN (packed not 16-byte aligned), BL_ERR_HIP.
+ */
+int pack_ternary_weights(const int8_t* w, uint8_t* packed, int N, int K,
+                         int32_t* n_invalid, hipStream_t stream);
+
+/*
+ * Host twin of pack_ternary_weights, bit-identical, for tooling and tests
+ * (no device needed).  Returns the number of invalid entries (>= 0) or a
+ * negative BL_ERR_* code.
+ */
+int64_t bl_pack_ternary_host(const int8_t* w_host, uint8_t* packed_host, int N, int K);
+
+/*
+ * quantize_act_absmax_i8 -- per-token (per-row) absmax int8 quantisation
+ * ([W2A8] §六 item 3):
+ *   s[m]    = 127 / max(max_k |x[m][k]|, 1e-5)          fp32, IEEE division
+ *   q[m][k] = clamp(round_half_even(x[m][k] * s[m]), -128, 127)
+ *   x        device, M x K, fp32 (x_dtype = 0) or bf16 (x_dtype = 1)
+ *   q        device, int8, M x K
+ *   s        device, fp32, M
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_ARG (x_dtype),
+ * BL_ERR_HIP.
+ */
+int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int M, int K,
+                           hipStream_t stream);
+
+/*
+ * bitlinear_i8xi2 -- the layer on int8 activations ([W2A8] §二 2.2, §5.3):
+ *   acc[m][n] = sum_k xq[m][k] * w[n][k]                       exact int32
+ *   y[m][n]   = bf16_rne( (double)acc[m][n] * ws[n / (N / ws_num)] / s[m] )
+ *   xq       device, int8, M x K row-major
+ *   packed   device, bl_packed_bytes(N, K) bytes, 64x64-tile layout
+ *   s        device, fp32, M activation scales (127 / amax of each row)
+ *   ws       device, bf16, ws_num weight scales, one per equal N-segment
+ *   ws_num   1 <= ws_num <= 64 and N % ws_num == 0
+ *   y        device, bf16, M x N row-major
+ *   acc      device, int32, M x N row-major, or NULL (not written)
+ * The activation scale divides: s = 127/amax quantised the activations, so
+ * y approximates x . w^T * ws.
+ * M == 1 runs the wavefront-per-64-rows GEMV (v_dot4 on unpacked bytes);
+ * M >= 2 runs the int8 MFMA kernel (v_mfma_i32_16x16x64_i8), 64 rows of M
+ * per workgroup column.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_ARG, BL_ERR_HIP.
+ */
+int bitlinear_i8xi2(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,
+                    int ws_num, uint16_t* y, int32_t* acc, int M, int N, int K,
+                    hipStream_t stream);
+
+/*
+ * bitlinear_bf16_i8xi2 -- quantise bf16 activations per token, then the
+ * layer, as one call ([W2A8] §六 item 3 followed by §5.3).  The result is
+ * bit-identical to quantize_act_absmax_i8 (bf16) followed by
+ * bitlinear_i8xi2.
+ *   x        device, bf16, M x K
+ *   q_out    device, int8, M x K, or NULL: the quantised activations
+ *   s_out    device, fp32, M, or NULL: the activation scales
+ *   acc      device, int32, M x N, or NULL
+ * M == 1: one fused kernel (each workgroup quantises the row into LDS).
+ * M >= 2: q_out and s_out are required (they are the staging buffers of a
+ * quantise kernel followed by the MFMA kernel); BL_ERR_NULL otherwise.
+ * Errors: as bitlinear_i8xi2.
+ */
+int bitlinear_bf16_i8xi2(const uint16_t* x, const uint8_t* packed, const uint16_t* ws,
+                         int ws_num, uint16_t* y, int8_t* q_out, float* s_out, int32_t* acc,
+                         int M, int N, int K, hipStream_t stream);
+
+/*
+ * Decode-step graph ([W2A8] §六 item 1: each decode step is a graph
+ * replay).  A bl_gemv_desc is one M = 1 call of bitlinear_bf16_i8xi2; the
+ * graph chains n of them in array order (each depends on the previous one)
+ * and is replayed with one launch.
+ */
+typedef struct bl_gemv_desc {
+    const uint16_t* x;       /* device, bf16, K */
+    const uint8_t* packed;   /* device, bl_packed_bytes(N, K) */
+    const uint16_t* ws;      /* device, bf16, ws_num */
+    int ws_num;
+    uint16_t* y;             /* device, bf16, N */
+    int32_t* acc;            /* device, int32, N, or NULL */
+    int N;
+    int K;
+} bl_gemv_desc;
+
+typedef struct bl_graph bl_graph;
+
+/*
+ * Capture the n calls (1 <= n <= 65536) on an internal stream and
+ * instantiate them.  The descriptors are validated first; the pointers they
+ * hold are baked into the graph and must stay valid while it exists.
+ * *out receives the graph (NULL on error).
+ * Errors: BL_ERR_NULL, BL_ERR_ARG (n), any error of bitlinear_bf16_i8xi2
+ * for an invalid descriptor, BL_ERR_HIP.
+ */
+int bl_graph_create(const bl_gemv_desc* descs, int n, bl_graph** out);
+
+/* Enqueue one replay of the graph on `stream`.  Errors: BL_ERR_NULL, BL_ERR_HIP. */
+int bl_graph_launch(bl_graph* graph, hipStream_t stream);
+
+/* Number of calls the graph holds, or BL_ERR_NULL. */
+int bl_graph_size(const bl_graph* graph);
+
+/* Destroy the graph (NULL is allowed).  The caller ensures no replay is in flight. */
+int bl_graph_destroy(bl_graph* graph);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,90 @@
+"""GPU parity of the batched (M >= 2) path on int8 MFMA against the oracle.
+
+The batched workload of the pages' model shapes (M in {16, 32, 64},
+N=13824, K=2560, per-row absmax quantisation of x ~ N(0,1) on the device),
+plus M that are not multiples of 16 or exceed one 64-row workgroup column,
+and ragged N and K.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import dev, bf16_dev, host_bits, assert_bf16_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bl():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import bit_gemv_bitlinear_amd as m
+    return m
+
+
+def check(bl, name, w, xq, s, ws_bits, ws_num):
+    import torch
+    M, K = xq.shape
+    N = w.shape[0]
+    print(f"mfma {name} M={M} N={N} K={K}", flush=True)
+    packed = bl.pack_ternary_weights(dev(w))
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = bl.bitlinear_i8xi2(dev(xq), packed, dev(s), bf16_dev(ws_bits), N, ws_num, acc=acc)
+    torch.cuda.synchronize()
+    acc_o, y_o = oracle.bitlinear_i8(xq, w, s, ws_bits, ws_num)
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_o)
+    assert assert_bf16_close(host_bits(y), y_o, max_ulp=1) == 0
+
+
+@pytest.mark.parametrize("M", synth.BATCHED_M)
+def test_batched_model_shape(bl, M):
+    import torch
+    c = synth.batched(M)
+    print(f"batched M={M}: quantise on the device", flush=True)
+    q, s = bl.quantize_act_absmax_i8(dev(c.x))
+    torch.cuda.synchronize()
+    qo, so = oracle.quant_absmax_i8(c.x)
+    np.testing.assert_array_equal(q.cpu().numpy(), qo)
+    np.testing.assert_array_equal(s.cpu().numpy(), so)
+    check(bl, c.name, c.w, qo, so, c.ws, c.ws_num)
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 64, 64), (15, 100, 208), (16, 64 * 3, 2560), (17, 130, 80),
+                                   (33, 640, 6912), (64, 256, 1024), (65, 192, 144),
+                                   (130, 70, 272), (64, 2560, 13824)])
+def test_shapes(bl, M, N, K):
+    c = synth.make_int8_gemv(f"m{M}", M, N, K, 1, synth.seed_for(8, 0, M + N % 89))
+    check(bl, c.name, c.w, c.xq, c.s, c.ws, c.ws_num)
+
+
+def test_extremes_and_segments(bl):
+    g = synth.rng(515)
+    M, N, K = 32, 64 * 4, 2560
+    w = synth.ternary_uniform(g, N, K)
+    w[:64] = 1
+    w[64:128] = -1
+    xq = synth.int8_uniform(g, M, K, -128, 127)
+    xq[0] = -128
+    xq[1] = 127
+    xq[2] = 0
+    s = synth.act_scale(g, M)
+    check(bl, "extremes_ws4", w, xq, s, synth.ws_bits(g, 4), 4)
+
+
+def test_bf16_entry_with_staging(bl):
+    import torch
+    M, N, K = 48, 640, 2560
+    c = synth.make_float_gemv("bf16_m48", M, N, K, 2, 2718, bf16=True)
+    print(f"mfma bf16 entry M={M}", flush=True)
+    packed = bl.pack_ternary_weights(dev(c.w))
+    q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    s = torch.empty((M,), dtype=torch.float32, device="cuda")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = bl.bitlinear_bf16_i8xi2(bf16_dev(c.x), packed, bf16_dev(c.ws), N, 2, q_out=q, s_out=s,
+                                acc=acc)
+    torch.cuda.synchronize()
+    qo, so, acc_o, y_o = oracle.bitlinear_bf16(c.x, c.w, c.ws, 2)
+    np.testing.assert_array_equal(q.cpu().numpy(), qo)
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_o)
+    np.testing.assert_array_equal(host_bits(y), y_o)
