@@ -55,7 +55,7 @@ int check_layer_bf16(const uint16_t* x, const uint8_t* packed, const uint16_t* w
     int rc = check_mnk(M, N, K);
     if (rc) return rc;
     if ((rc = check_ws(ws_num, N))) return rc;
-    const bool staged = (M > 1) || (K > bl::kFusedMaxK);
+    const bool staged = (M > 1) || (K > bl::kGemvMaxK);
     if (staged && (!q_out || !s_out)) return BL_ERR_NULL;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(ws, 2) || !aligned(y, 2) ||
         (q_out && !aligned(q_out, 16)) || (s_out && !aligned(s_out, 4)) ||
@@ -66,7 +66,7 @@ int check_layer_bf16(const uint16_t* x, const uint8_t* packed, const uint16_t* w
 
 int run_layer_i8(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,
                  int ws_num, uint16_t* y, int32_t* acc, int M, int N, int K, hipStream_t stream) {
-    if (M == 1)
+    if (M == 1 && K <= bl::kGemvMaxK)
         return status_of(bl::launch_gemv_i8(xq, packed, s, ws, ws_num, y, acc, N, K, stream));
     return status_of(bl::launch_gemm_mfma(xq, packed, s, ws, ws_num, y, acc, M, N, K, stream));
 }
@@ -74,7 +74,7 @@ int run_layer_i8(const int8_t* xq, const uint8_t* packed, const float* s, const 
 int run_layer_bf16(const uint16_t* x, const uint8_t* packed, const uint16_t* ws, int ws_num,
                    uint16_t* y, int8_t* q_out, float* s_out, int32_t* acc, int M, int N, int K,
                    hipStream_t stream) {
-    if (M == 1 && K <= bl::kFusedMaxK)
+    if (M == 1 && K <= bl::kGemvMaxK)
         return status_of(bl::launch_gemv_bf16_fused(x, packed, ws, ws_num, y, q_out, s_out, acc,
                                                     N, K, stream));
     int rc = status_of(bl::launch_quant(x, 1, q_out, s_out, M, K, stream));

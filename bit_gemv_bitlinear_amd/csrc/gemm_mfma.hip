@@ -12,10 +12,11 @@
 //     wavefronts that split the K steps of the band between them;
 //   * per K step (64 K) a wavefront reads the band's 1 KiB tile as four
 //     4-byte-per-lane loads of 256 contiguous bytes: lane (j = lane%16,
-//     g = lane/16) takes word g of row slot 16t + j, which is exactly the
-//     B operand of v_mfma_i32_16x16x64_i8 for row tile t (16 K of one
-//     column); v_perm_b32 turns the 2-bit codes into signed int8 weights
-//     (code 0, the padding, becomes 0) after each shift-and-mask of [W2A8] §5.2;
+//     g = lane/16) takes the word of row 16t + j for K chunk g (word
+//     64t + 16*(j/4) + 4g + j%4 of the tile), which is exactly the B operand
+//     of v_mfma_i32_16x16x64_i8 for row tile t (16 K of one column);
+//     v_perm_b32 turns the 2-bit codes into signed int8 weights (code 0, the
+//     padding, becomes 0) after each shift-and-mask of [W2A8] §5.2;
 //   * the A operand (16 rows m x 64 K) is read straight from the int8
 //     activations, 16 bytes per lane, zero outside M and K;
 //   * the four wavefronts' int32 tiles are added with LDS atomics (exact in
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
         const uint32_t* tile = band_words + static_cast<size_t>(st) * (kTileBytes / 4);
         uint32_t bw[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bw[t] = __builtin_nontemporal_load(tile + (16 * t + j) * 4 + g);
+        for (int t = 0; t < 4; ++t)
+            bw[t] = __builtin_nontemporal_load(tile + 64 * t + 16 * (j >> 2) + 4 * g + (j & 3));
         v4i a[MT];
         const int k = st * kTileK + 16 * g;
 #pragma unroll

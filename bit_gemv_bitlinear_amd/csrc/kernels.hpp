@@ -18,13 +18,22 @@ int64_t pack_host(const int8_t* w, uint8_t* packed, int N, int K);
 hipError_t launch_quant(const void* x, int x_is_bf16, int8_t* q, float* s, int M, int K,
                         hipStream_t stream);
 
-// M == 1, int8 activations.
+// M == 1 GEMV geometry: `waves` wavefronts per workgroup, `steps` K steps
+// (64 K each) per wavefront; waves == 0 when K is beyond the GEMV kernels
+// (K > kGemvMaxK), which then leave M == 1 to the MFMA kernel.
+struct GemvShape {
+    int waves;
+    int steps;
+};
+constexpr int kGemvMaxK = 64 * 16 * 20;
+GemvShape gemv_shape(int K);
+
+// M == 1, int8 activations; K <= kGemvMaxK.
 hipError_t launch_gemv_i8(const int8_t* xq, const uint8_t* packed, const float* s,
                           const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int N, int K,
                           hipStream_t stream);
 
-// M == 1, bf16 activations quantised inside the kernel; K <= kFusedMaxK.
-constexpr int kFusedMaxK = 65536;
+// M == 1, bf16 activations quantised inside the kernel; K <= kGemvMaxK.
 hipError_t launch_gemv_bf16_fused(const uint16_t* x, const uint8_t* packed, const uint16_t* ws,
                                   int ws_num, uint16_t* y, int8_t* q_out, float* s_out,
                                   int32_t* acc, int N, int K, hipStream_t stream);

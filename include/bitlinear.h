@@ -43,16 +43,18 @@
  *   The weight w[n][k] of an N x K matrix (row n produces output n) is the
  *   2-bit code w + 2 ({-1,0,1} -> {1,2,3}, [W2A8] §5.2).  Code 0 marks
  *   padding.  With S = ceil(K/64) steps and ceil(N/64) bands:
- *     tile  t = (n / 64) * S + k / 64          1024 bytes per tile
- *     byte  t*1024 + 16*(n % 64) + 4*((k % 64) / 16) + (k % 16) % 4
+ *     tile  t = (n / 64) * S + k / 64                    1024 bytes per tile
+ *     slot  q = 4 * ((n % 64) / 4) + (k % 64) / 16       16 bytes per slot
+ *     byte  t*1024 + 16*q + 4*(n % 4) + (k % 16) % 4
  *     bits  2*((k % 16) / 4) and the next one
- *   i.e. a tile is 64 rows x 64 K; row slot r holds 16 bytes = four 32-bit
- *   words of 16 consecutive K each, and inside a word element e sits at bit
- *   8*(e%4) + 2*(e/4): the page's interleave 0,4,8,12,1,5,... ([W2A8] §5.2),
- *   so (word >> 2i) & 0x03030303 holds elements 4i..4i+3 as bytes.  Lane r of
- *   a 64-wide wavefront reads row slot r with one 16-byte load, and a
- *   wavefront's load of a tile is 1 KiB contiguous.  Rows n >= N and columns
- *   k >= K of the last tiles are code 0.
+ *   i.e. a tile is 64 rows x 64 K; slot q holds four 32-bit words, rows
+ *   4*(q/4) .. +3 of the 16-wide K chunk q%4; inside a word element e sits at
+ *   bit 8*(e%4) + 2*(e/4): the page's interleave 0,4,8,12,1,5,... ([W2A8]
+ *   §5.2), so (word >> 2i) & 0x03030303 holds elements 4i..4i+3 as bytes.
+ *   Lane l of a 64-wide wavefront reads slot l with one 16-byte load (a
+ *   wavefront's load of a tile is 1 KiB contiguous) and needs one 16-byte
+ *   run of activations for it.  Rows n >= N and columns k >= K of the last
+ *   tiles are code 0.
  */
 #ifndef BITLINEAR_H
 #define BITLINEAR_H
@@ -137,9 +139,9 @@ int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int 
  *   acc      device, int32, M x N row-major, or NULL (not written)
  * The activation scale divides: s = 127/amax quantised the activations, so
  * y approximates x . w^T * ws.
- * M == 1 runs the wavefront-per-64-rows GEMV (v_dot4 on unpacked bytes);
- * M >= 2 runs the int8 MFMA kernel (v_mfma_i32_16x16x64_i8), 64 rows of M
- * per workgroup column.
+ * M == 1 with K <= 20480 runs the GEMV kernel (one workgroup per 64 output
+ * rows, v_dot4 on masked codes); M >= 2, or K > 20480, runs the int8 MFMA
+ * kernel (v_mfma_i32_16x16x64_i8), 64 rows of M per workgroup column.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_ARG, BL_ERR_HIP.
  */
 int bitlinear_i8xi2(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,
@@ -155,9 +157,10 @@ int bitlinear_i8xi2(const int8_t* xq, const uint8_t* packed, const float* s, con
  *   q_out    device, int8, M x K, or NULL: the quantised activations
  *   s_out    device, fp32, M, or NULL: the activation scales
  *   acc      device, int32, M x N, or NULL
- * M == 1: one fused kernel (each workgroup quantises the row into LDS).
- * M >= 2: q_out and s_out are required (they are the staging buffers of a
- * quantise kernel followed by the MFMA kernel); BL_ERR_NULL otherwise.
+ * M == 1 and K <= 20480: one fused kernel (each workgroup quantises the row
+ * into LDS).  M >= 2 or K > 20480: q_out and s_out are required (they are
+ * the staging buffers of a quantise kernel followed by the layer kernel);
+ * BL_ERR_NULL otherwise.
  * Errors: as bitlinear_i8xi2.
  */
 int bitlinear_bf16_i8xi2(const uint16_t* x, const uint8_t* packed, const uint16_t* ws,
@@ -184,8 +187,8 @@ typedef struct bl_gemv_desc {
 typedef struct bl_graph bl_graph;
 
 /*
- * Capture the n calls (1 <= n <= 65536) on an internal stream and
- * instantiate them.  The descriptors are validated first; the pointers they
+ * Capture the n calls (1 <= n <= 65536; every descriptor K <= 20480) on an
+ * internal stream and instantiate them.  The descriptors are validated first; the pointers they
  * hold are baked into the graph and must stay valid while it exists.
  * *out receives the graph (NULL on error).
  * Errors: BL_ERR_NULL, BL_ERR_ARG (n), any error of bitlinear_bf16_i8xi2

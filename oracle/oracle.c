@@ -198,13 +198,14 @@ size_t oracle_packed_bytes(int N, int K)
  * N x K matrix (row n = output n) is stored as the 2-bit code w + 2
  * ({-1,0,1} -> {1,2,3}, as on [W2A8] §5.2); the code lives in
  *   tile      t = (n / 64) * ceil(K/64) + (k / 64)       (1024 bytes each)
- *   row slot  r = n % 64                                  (16 bytes each)
- *   word      d = (k % 64) / 16                           (4 bytes each, little endian)
+ *   slot      q = 4 * ((n % 64) / 4) + (k % 64) / 16     (16 bytes each)
+ *   word      i = n % 4                                  (4 bytes each, little endian)
  *   element   e = k % 16
- *   byte      t*1024 + 16*r + 4*d + (e % 4)
+ *   byte      t*1024 + 16*q + 4*i + (e % 4)
  *   bits      2*(e / 4) .. 2*(e / 4) + 1 of that byte
- * so inside each 32-bit word element e sits at bit 8*(e%4) + 2*(e/4): the
- * word holds its 16 elements in the page's interleaved order
+ * so a 16-byte slot holds four rows (4*((n%64)/4) .. +3) of one 16-wide K
+ * chunk, and inside each 32-bit word element e sits at bit 8*(e%4) + 2*(e/4):
+ * the word holds its 16 elements in the page's interleaved order
  * 0,4,8,12,1,5,9,13,2,6,10,14,3,7,11,15 ([W2A8] §5.2).
  * Positions with n >= N or k >= K (padding of the last tile row/column)
  * hold code 0.  Code 0 at a real position is an error.
@@ -222,10 +223,10 @@ int oracle_unpack_r64(const uint8_t* packed, int N, int K, int8_t* w, int64_t* b
     for (int n = 0; n < N; ++n) {
         for (int k = 0; k < K; ++k) {
             size_t t = (size_t)(n / 64) * steps + (size_t)(k / 64);
-            size_t r = (size_t)(n % 64);
-            size_t d = (size_t)((k % 64) / 16);
+            size_t q = 4 * (size_t)((n % 64) / 4) + (size_t)((k % 64) / 16);
+            size_t i = (size_t)(n % 4);
             int e = k % 16;
-            size_t byte = t * 1024 + 16 * r + 4 * d + (size_t)(e % 4);
+            size_t byte = t * 1024 + 16 * q + 4 * i + (size_t)(e % 4);
             int bit = 2 * (e / 4);
             int code = (packed[byte] >> bit) & 3;
             if (code == 0) {
@@ -246,8 +247,9 @@ int oracle_unpack_r64(const uint8_t* packed, int N, int K, int8_t* w, int64_t* b
                     if (n < (size_t)N && k < (size_t)K)
                         continue;
                     size_t t = band * steps + st;
-                    int d = kk / 16, e = kk % 16;
-                    size_t byte = t * 1024 + 16 * (size_t)r + 4 * (size_t)d + (size_t)(e % 4);
+                    size_t q = 4 * (size_t)(r / 4) + (size_t)(kk / 16);
+                    int e = kk % 16;
+                    size_t byte = t * 1024 + 16 * q + 4 * (size_t)(r % 4) + (size_t)(e % 4);
                     int code = (packed[byte] >> (2 * (e / 4))) & 3;
                     if (code != 0) {
                         if (bad)

@@ -104,7 +104,7 @@ def test_bitlinear_bf16_errors():
     assert _bf(x=None) == bl.BL_ERR_NULL
     assert _bf(M=2) == bl.BL_ERR_NULL                    # M > 1 needs the staging buffers
     assert _bf(M=2, q=A) == bl.BL_ERR_NULL
-    assert _bf(K=65536 + 16) == bl.BL_ERR_NULL           # beyond the fused K limit
+    assert _bf(K=20480 + 16) == bl.BL_ERR_NULL           # beyond the fused K limit
     assert _bf(K=40) == bl.BL_ERR_SHAPE
     assert _bf(ws_num=2, N=65) == bl.BL_ERR_ARG
     assert _bf(x=A + 8) == bl.BL_ERR_ALIGN

@@ -100,7 +100,8 @@ def test_tiled_words_decode_the_page_way():
     for n in (0, 1, 63, 64, 100, 127):
         for k0 in range(0, K, 16):
             tile = (n // 64) * steps + k0 // 64
-            word_index = (tile * 1024 + 16 * (n % 64) + 4 * ((k0 % 64) // 16)) // 4
+            slot = 4 * ((n % 64) // 4) + (k0 % 64) // 16
+            word_index = (tile * 1024 + 16 * slot + 4 * (n % 4)) // 4
             assert pl.decode_word(int(words[word_index])) == w[n, k0:k0 + 16].tolist()
 
 
@@ -115,7 +116,8 @@ def test_padding_layout_and_errors():
         for k in range(K):
             t = (n // 64) * 2 + k // 64
             e = k % 16
-            off = t * 1024 + 16 * (n % 64) + 4 * ((k % 64) // 16) + e % 4
+            slot = 4 * ((n % 64) // 4) + (k % 64) // 16
+            off = t * 1024 + 16 * slot + 4 * (n % 4) + e % 4
             p[off] |= 2 << (2 * (e // 4))
     assert (oracle.unpack_r64(p, N, K) == 0).all()
     bad = p.copy()
