@@ -54,11 +54,51 @@ __device__ __forceinline__ uint16_t bf16_from_double_rne(double v) {
 
 // The epilogue of [W2A8] §5.3 under the reading y = acc * ws / s: the
 // activation scale s = 127/amax multiplied x on the way in, so it divides
-// here.  Evaluated in fp64 ((acc * ws) is exact; one rounding for the
-// quotient) and rounded once to bf16.
+// here.  The result is bf16_rne(fl64(acc * ws) / s) -- the product is exact,
+// the quotient is rounded once to fp64, then once to bf16.
 __device__ __forceinline__ uint16_t epilogue_bf16(int32_t acc, float ws, float s) {
     const double v = (static_cast<double>(acc) * static_cast<double>(ws)) / static_cast<double>(s);
     return bf16_from_double_rne(v);
+}
+
+// bf16 rounding of an fp64 value in bf16's normal range, on the two 32-bit
+// halves of its encoding: the 7 kept fraction bits are bits 13..19 of the
+// high word, the round bit is bit 12, the sticky bits are the rest.  Returns
+// false -- leaving the value to the general path -- outside the normal range
+// (zero excepted) and when the value lies within 64 units of its last bit of
+// a rounding boundary.
+__device__ __forceinline__ bool bf16_rne_fast(double v, uint16_t& out) {
+    const uint32_t hi = static_cast<uint32_t>(__double2hiint(v));
+    const uint32_t lo = static_cast<uint32_t>(__double2loint(v));
+    const uint32_t sign = (hi >> 16) & 0x8000u;
+    const uint32_t exp = (hi >> 20) & 0x7FFu;
+    const uint32_t low13 = hi & 0x1FFFu;
+    const uint32_t mant7 = (hi >> 13) & 0x7Fu;
+    const uint32_t round = (hi >> 12) & 1u;
+    const uint32_t sticky = ((hi & 0xFFFu) | lo) != 0u;
+    const uint32_t up = round & (sticky | (mant7 & 1u));
+    // carries into the exponent when the fraction overflows (to inf from the
+    // top binade, as round-to-nearest requires)
+    const uint32_t bits = ((exp - 896u) << 7) + mant7 + up;
+    const bool zero = ((hi & 0x7FFFFFFFu) | lo) == 0u;
+    const bool normal = (exp >= 897u) && (exp <= 1150u);
+    const bool near = (low13 == 0x1000u && lo <= 64u) || (low13 == 0x0FFFu && lo >= 0xFFFFFFC0u);
+    out = static_cast<uint16_t>(sign | (zero ? 0u : bits));
+    return zero || (normal && !near);
+}
+
+// The same value as epilogue_bf16 without a division on the common path:
+// inv_s = fl64(1/s) is computed once per kernel, and p * inv_s lies within
+// 2^-51 (relative) of the fp64 quotient, i.e. within 4 units of its last
+// bit.  Its bf16 rounding is therefore the quotient's unless it sits within
+// 64 units of a rounding boundary (or outside bf16's normal range), in which
+// case the quotient itself is computed and rounded.
+__device__ __forceinline__ uint16_t epilogue_bf16_fast(int32_t acc, float ws, float s,
+                                                       double inv_s) {
+    const double p = static_cast<double>(acc) * static_cast<double>(ws);   // exact
+    uint16_t out;
+    if (!bf16_rne_fast(p * inv_s, out)) out = bf16_from_double_rne(p / static_cast<double>(s));
+    return out;
 }
 
 // Per-activation quantisation of [W2A8] §六 item 3: round half to even of

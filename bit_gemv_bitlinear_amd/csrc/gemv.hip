@@ -27,7 +27,9 @@
 //     term removing the +2 offset (padding code 0 contributes nothing);
 //   * the 4 lanes sharing a K step exchange partial sums with DPP so that
 //     lane r ends with row r; the W wavefronts' sums are added through LDS;
-//     the epilogue runs in fp64 and rounds once to bf16.
+//     the epilogue multiplies by a precomputed fp64 1/s and rounds once to
+//     bf16, dividing only when the product lies next to a rounding boundary
+//     (so the result is that of the exact fp64 division).
 #include <array>
 #include <utility>
 
@@ -124,13 +126,14 @@ __device__ __forceinline__ int sum_i8x4(uint32_t d, int acc) {
     return dot4(static_cast<int>(d), 0x01010101, acc);
 }
 
+// seg = N / ws_num: rows per weight scale.
 // FUSED = false: xin is int8 activations with scale s_in[0].
 // FUSED = true:  xin is bf16; the workgroup quantises it (per-token absmax,
 //                [W2A8] §六 item 3); workgroup 0 writes q_out / s_out if given.
 template <int P, bool FUSED>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     const void* __restrict__ xin, const v4u* __restrict__ packed, const float* __restrict__ s_in,
-    const uint16_t* __restrict__ ws, int ws_num, uint16_t* __restrict__ y,
+    const uint16_t* __restrict__ ws, int seg, uint16_t* __restrict__ y,
     int32_t* __restrict__ acc, int8_t* __restrict__ q_out, float* __restrict__ s_out, int N,
     int K) {
     extern __shared__ int4 act[];   // W*P*4 16-byte chunks: the int8 row, zero-padded
@@ -148,8 +151,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     const int n16 = K >> 4;        // 16-byte chunks of int8 activations
     const int padded16 = W * P * 4;
 
-    // 1. The activation row first (so that waiting for it does not wait for
-    //    the weights), then every weight load of this wavefront.
+    // 1. The activation row and this lane's weight scale first (so that
+    //    waiting for them does not wait for the weights), then every weight
+    //    load of this wavefront.
+    const int n = band * 64 + lane;
+    const uint16_t wsb = ws[min(n, N - 1) / seg];   // unconditional: no branch, no early wait
     uint4 xv[kCached];
     const int n_in = FUSED ? (K >> 3) : n16;   // 16-byte input chunks
     const uint4* x16 = reinterpret_cast<const uint4*>(xin);
@@ -214,6 +220,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
         if (band == 0 && s_out != nullptr && tid == 0) s_out[0] = sm;
     }
     for (int i = n16 + tid; i < padded16; i += nthreads) act[i] = make_int4(0, 0, 0, 0);
+    // 1/s for the epilogue, computed here while the weights are in flight;
+    // the empty asm statement keeps the compiler from sinking the division
+    // past the barriers to its use.
+    double inv_s = 1.0 / static_cast<double>(sm);
+    asm volatile("" : "+v"(inv_s));
     xs = wave_sum(xs);
     if (lane == 0) xsum_sh[wave] = xs;
     __syncthreads();
@@ -240,9 +251,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
             xsum += xsum_sh[i];
         }
         total -= 2 * xsum;
-        const int n = band * 64 + lane;
         if (n < N) {
-            y[n] = epilogue_bf16(total, bf16_to_float(ws[n / (N / ws_num)]), sm);
+            y[n] = epilogue_bf16_fast(total, bf16_to_float(wsb), sm, inv_s);
             if (acc) acc[n] = total;
         }
     }
@@ -272,7 +282,7 @@ hipError_t launch(bool fused, const void* x, const uint8_t* packed, const float*
     const size_t lds = static_cast<size_t>(g.waves) * g.steps * kTileK;
     const GemvFn fn = fused ? kBf16Kernels[g.steps - 1] : kI8Kernels[g.steps - 1];
     fn<<<bands, g.waves * 64, lds, stream>>>(x, reinterpret_cast<const v4u*>(packed), s, ws,
-                                            ws_num, y, acc, q_out, s_out, N, K);
+                                            N / ws_num, y, acc, q_out, s_out, N, K);
     return hipGetLastError();
 }
 

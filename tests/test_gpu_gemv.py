@@ -157,3 +157,53 @@ def test_fused_without_optional_outputs(bl):
     torch.cuda.synchronize()
     _, _, _, y_o = oracle.bitlinear_bf16(c.x, c.w, c.ws, 1)
     np.testing.assert_array_equal(host_bits(y), y_o)
+
+
+def _rows_with_sums(targets, K):
+    """Ternary rows whose dot product with x (x[k] = 2^(k % 7), groups of 7) equals targets[n]."""
+    x = np.zeros((1, K), dtype=np.int8)
+    groups = K // 7
+    for g in range(groups):
+        for b in range(7):
+            x[0, 7 * g + b] = 1 << b
+    w = np.zeros((len(targets), K), dtype=np.int8)
+    for n, t in enumerate(targets):
+        sign = 1 if t >= 0 else -1
+        rem = abs(int(t))
+        for g in range(groups):
+            c = min(rem, 127)
+            rem -= c
+            for b in range(7):
+                if (c >> b) & 1:
+                    w[n, 7 * g + b] = sign
+        assert rem == 0
+    return w, x
+
+
+@pytest.mark.parametrize("s_val", [3.0, 1.0, 7.0, 127.0 / 3.3])
+def test_epilogue_rounding_boundaries(bl, s_val):
+    # outputs that land exactly on (or next to) bf16 midpoints: the division-free
+    # epilogue must fall back to the exact quotient there (e.g. 777 / 3 = 259 -> 260)
+    K = 64 * 4
+    base = [257, 259, 261, 383, 385, 511, 513, 515, 1025, 1027, 2047, 2049]
+    targets = []
+    for t in base:
+        for d in (-1, 0, 1):
+            v = int(round(t * s_val)) + d
+            if abs(v) <= (K // 7) * 127:
+                targets += [v, -v]
+    targets = targets[:128] + [0] * max(0, 128 - len(targets))
+    w, x = _rows_with_sums(targets, K)
+    check_i8(bl, f"midpoints_s{s_val:.4f}", w, x, np.array([s_val], np.float32),
+             np.array([0x3F80], np.uint16), 1)
+
+
+@pytest.mark.parametrize("s_val", [1e-36, 3e38, 1e37])
+def test_epilogue_outside_normal_range(bl, s_val):
+    # outputs that overflow to +-inf (s = 1e-36) or fall into bf16 subnormals (s >= 1e37)
+    K = 64 * 4
+    t = [0, 1, 2, 3, 5, 100, 339, 340, 341, 500, 1000, 2000, 4000]
+    targets = t + [-v for v in t if v]
+    w, x = _rows_with_sums(targets, K)
+    check_i8(bl, f"extreme_s{s_val:g}", w, x, np.array([s_val], np.float32),
+             np.array([0x3F80], np.uint16), 1)
