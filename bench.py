@@ -41,7 +41,9 @@ PEAK_INT8_TOPS = 5000.0          # MI355X dense int8 MFMA, published peak (TOP/s
 A100_W2A8_GBS_13824x2560 = 473.5  # the page's 18.75 us on A100 (§7.1), as GB/s by the same formula
 CACHE_DEFEAT_BYTES = 512 << 20
 PROFILE_PMC = os.path.join(ROOT, "profiles", "gemv_i8_13824x2560_pmc.txt")
-GEMV_SOURCE = os.path.join(ROOT, "bit_gemv_bitlinear_amd", "csrc", "gemv.hip")
+GEMV_SOURCES = [os.path.join(ROOT, "bit_gemv_bitlinear_amd", "csrc", f)
+                for f in ("gemv.hip", "common.hpp")]
+PROBE_LIB = os.path.join(ROOT, "bit_gemv_bitlinear_amd", "libstream_floor.so")
 
 
 def gemv_bytes(M, N, K, ws_num, x_bytes=1):
@@ -128,7 +130,7 @@ def headline(bl, steps, warmup):
             raise RuntimeError(f"bitlinear_i8xi2 failed: {rc}")
 
     ms = time_graph(launch, steps, warmup)
-    return c, ms, n_copies
+    return c, ms, n_copies, copies
 
 
 def fused(bl, steps, warmup):
@@ -282,6 +284,13 @@ def cpu_baseline(seconds):
                       f"sums, fp64 epilogue), single-threaded C, {el:.1f} s"}
 
 
+def gemv_source_sha256():
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def pmc_traffic():
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it is for this kernel source."""
     if not os.path.exists(PROFILE_PMC):
@@ -291,10 +300,55 @@ def pmc_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    src = hashlib.sha256(open(GEMV_SOURCE, "rb").read()).hexdigest()
-    if vals.get("gemv_source_sha256") != src or "traffic_bytes_per_launch" not in vals:
+    if vals.get("gemv_source_sha256") != gemv_source_sha256() or "traffic_bytes_per_launch" not in vals:
         return None
     return float(vals["traffic_bytes_per_launch"])
+
+
+def gemv_geometry(K):
+    """Wavefronts x K-steps per workgroup that the library's M=1 GEMV uses for this K
+    (the same rule as gemv_shape in bit_gemv_bitlinear_amd/csrc/gemv.hip)."""
+    S = -(-K // 64)
+    best, best_key = None, None
+    for W in range(16, 0, -1):
+        P = -(-S // W)
+        if P > 20:
+            continue
+        key = (-(-W // 4) * P, W * P - S)
+        if best_key is None or key < best_key:
+            best, best_key = (W, P), key
+    return best
+
+
+def stream_floor(copies, N, K, steps, warmup):
+    """Same launch shape and bytes as the GEMV: an empty launch and a pure streaming read."""
+    import ctypes
+    torch = _torch()
+    lib = ctypes.CDLL(PROBE_LIB)
+    P_ = ctypes.c_void_p
+    I_ = ctypes.c_int
+    lib.stream_floor_empty.argtypes = [I_, I_, P_, P_]
+    lib.stream_floor_read.argtypes = [P_, I_, I_, I_, I_, P_, P_]
+    bands, S = -(-N // 64), -(-K // 64)
+    W, P = gemv_geometry(K)
+    out = torch.zeros(bands, dtype=torch.int32, device="cuda")
+    ptrs = [c.data_ptr() for c in copies]
+
+    def empty(i):
+        if lib.stream_floor_empty(bands, W, out.data_ptr(), torch.cuda.current_stream().cuda_stream):
+            raise RuntimeError("stream_floor_empty failed")
+
+    def read(i):
+        if lib.stream_floor_read(ptrs[i % len(ptrs)], bands, S, W, P, out.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream):
+            raise RuntimeError("stream_floor_read failed")
+
+    e_ms = time_graph(empty, steps, warmup)
+    r_ms = time_graph(read, steps, warmup)
+    nbytes = bands * S * 1024
+    return {"launch_shape": f"{bands} workgroups x {W} wavefronts, {P} 16-byte loads per lane",
+            "empty_launch_us": round(e_ms * 1e3, 3), "stream_read_us": round(r_ms * 1e3, 3),
+            "stream_read_GBps": round(nbytes / (r_ms * 1e-3) / 1e9, 1)}
 
 
 def main():
@@ -319,10 +373,15 @@ def main():
         sys.exit(2)
     import bit_gemv_bitlinear_amd as bl
 
-    c, ms, n_copies = headline(bl, args.steps, args.warmup)
+    c, ms, n_copies, copies = headline(bl, args.steps, args.warmup)
     nbytes = gemv_bytes(1, c.N, c.K, c.ws_num)
     gbs = nbytes / (ms * 1e-3) / 1e9
     detail = {}
+    if os.path.exists(PROBE_LIB) and not args.pmc_calibrate:
+        fl = stream_floor(copies, c.N, c.K, args.steps, args.warmup)
+        fl["gemv_us_over_stream_read_us"] = round(ms * 1e3 / fl["stream_read_us"], 3)
+        detail["single_launch_floor_13824x2560"] = fl
+    del copies
     if args.pmc_calibrate:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
