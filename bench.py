@@ -305,19 +305,19 @@ def pmc_traffic():
     return float(vals["traffic_bytes_per_launch"])
 
 
-def gemv_geometry(K):
-    """Wavefronts x K-steps per workgroup that the library's M=1 GEMV uses for this K
-    (the same rule as gemv_shape in bit_gemv_bitlinear_amd/csrc/gemv.hip)."""
-    S = -(-K // 64)
-    best, best_key = None, None
-    for W in range(16, 0, -1):
-        P = -(-S // W)
-        if P > 20:
-            continue
-        key = (-(-W // 4) * P, W * P - S)
-        if best_key is None or key < best_key:
-            best, best_key = (W, P), key
-    return best
+def gemv_geometry(N, K):
+    """(bands per workgroup, wavefronts per workgroup, K-steps per wavefront) of the library's
+    M=1 GEMV for this shape (the same rule as gemv_shape in bit_gemv_bitlinear_amd/csrc/gemv.hip)."""
+    S = -(-K // 256)
+    nbands = -(-N // 16)
+    Wb = 1
+    while Wb < 16 and -(-S // Wb) > 9:
+        Wb *= 2
+    P = -(-S // Wb)
+    B = 4
+    while B > 1 and (nbands // B < 200 or B * Wb > 16):
+        B //= 2
+    return B, B * Wb, P
 
 
 def stream_floor(copies, N, K, steps, warmup):
@@ -328,25 +328,26 @@ def stream_floor(copies, N, K, steps, warmup):
     P_ = ctypes.c_void_p
     I_ = ctypes.c_int
     lib.stream_floor_empty.argtypes = [I_, I_, P_, P_]
-    lib.stream_floor_read.argtypes = [P_, I_, I_, I_, I_, P_, P_]
-    bands, S = -(-N // 64), -(-K // 64)
-    W, P = gemv_geometry(K)
-    out = torch.zeros(bands, dtype=torch.int32, device="cuda")
+    lib.stream_floor_read.argtypes = [P_, I_, I_, I_, I_, I_, P_, P_]
+    nbands, S = -(-N // 16), -(-K // 256)
+    B, W, P = gemv_geometry(N, K)
+    groups = -(-nbands // B)
+    out = torch.zeros(groups, dtype=torch.int32, device="cuda")
     ptrs = [c.data_ptr() for c in copies]
 
     def empty(i):
-        if lib.stream_floor_empty(bands, W, out.data_ptr(), torch.cuda.current_stream().cuda_stream):
+        if lib.stream_floor_empty(groups, W, out.data_ptr(), torch.cuda.current_stream().cuda_stream):
             raise RuntimeError("stream_floor_empty failed")
 
     def read(i):
-        if lib.stream_floor_read(ptrs[i % len(ptrs)], bands, S, W, P, out.data_ptr(),
+        if lib.stream_floor_read(ptrs[i % len(ptrs)], nbands, S, B, W, P, out.data_ptr(),
                                  torch.cuda.current_stream().cuda_stream):
             raise RuntimeError("stream_floor_read failed")
 
     e_ms = time_graph(empty, steps, warmup)
     r_ms = time_graph(read, steps, warmup)
-    nbytes = bands * S * 1024
-    return {"launch_shape": f"{bands} workgroups x {W} wavefronts, {P} 16-byte loads per lane",
+    nbytes = nbands * S * 1024
+    return {"launch_shape": f"{groups} workgroups x {W} wavefronts ({B} bands), {P} 16-byte loads per lane",
             "empty_launch_us": round(e_ms * 1e3, 3), "stream_read_us": round(r_ms * 1e3, 3),
             "stream_read_GBps": round(nbytes / (r_ms * 1e-3) / 1e9, 1)}
 

@@ -17,6 +17,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
 BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP, BL_ERR_ARG = 0, -1, -2, -3, -4, -5
+# Largest K the single-kernel M = 1 paths take (include/bitlinear.h); beyond it the
+# bf16 entry needs staging buffers for the quantised activations.
+GEMV_MAX_K = 61440
 
 # Entry points declared in include/bitlinear.h: name -> (restype, argtypes).
 _P = ctypes.c_void_p
@@ -103,7 +106,7 @@ def bl_packed_bytes(N: int, K: int) -> int:
 
 
 def pack_ternary_weights(w, n_invalid=None):
-    """Pack an int8 N x K ternary matrix (device) into the 64x64-tile layout (uint8 tensor)."""
+    """Pack an int8 N x K ternary matrix (device) into the 16x256-tile layout (uint8 tensor)."""
     import torch
     _require(w, torch.int8, "w")
     N, K = w.shape
@@ -184,9 +187,9 @@ def bitlinear_bf16_i8xi2(x, packed, ws, N, ws_num=None, y=None, q_out=None, s_ou
     ws_num = ws.numel() if ws_num is None else ws_num
     if packed.numel() != bl_packed_bytes(N, K):
         raise ValueError("packed has the wrong size for (N, K)")
-    if (M > 1 or K > 65536) and q_out is None:
+    if (M > 1 or K > GEMV_MAX_K) and q_out is None:
         q_out = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    if (M > 1 or K > 65536) and s_out is None:
+    if (M > 1 or K > GEMV_MAX_K) and s_out is None:
         s_out = torch.empty((M,), dtype=torch.float32, device=x.device)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)

@@ -8,10 +8,11 @@
 
 namespace bl {
 
-// Geometry of the packed layout: a tile is 64 rows x 64 K = 1024 bytes; row
-// slot r of a tile is 16 bytes = four 32-bit words of 16 consecutive K.
-constexpr int kTileRows = 64;
-constexpr int kTileK = 64;
+// Geometry of the packed layout: a tile is 16 rows x 256 K = 1024 bytes; its
+// 16-byte slot q holds four 32-bit words, rows 4*(q/16) .. +3 of the 16-wide
+// K chunk q%16.
+constexpr int kTileRows = 16;
+constexpr int kTileK = 256;
 constexpr int kTileBytes = 1024;
 
 // Table for v_perm_b32: byte c of this word is the int8 weight of 2-bit code

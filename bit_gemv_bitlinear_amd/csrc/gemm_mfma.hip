@@ -8,13 +8,14 @@
 // for M >= 16 the layer is a dense contraction.
 //
 // Mapping (this library's design):
-//   * workgroup (band, mchunk): 64 output rows n x up to 64 rows m, 4
-//     wavefronts that split the K steps of the band between them;
-//   * per K step (64 K) a wavefront reads the band's 1 KiB tile as four
-//     4-byte-per-lane loads of 256 contiguous bytes: lane (j = lane%16,
-//     g = lane/16) takes the word of row 16t + j for K chunk g (word
-//     64t + 16*(j/4) + 4g + j%4 of the tile), which is exactly the B operand
-//     of v_mfma_i32_16x16x64_i8 for row tile t (16 K of one column);
+//   * workgroup (column, mchunk): four 16-row bands = 64 output rows n x up
+//     to 64 rows m, 4 wavefronts that split the K steps (64 K each) between
+//     them;
+//   * per K step a wavefront reads, for each of the four bands t, one word per
+//     lane: lane (j = lane%16, g = lane/16) takes the word of row j for the
+//     16-wide K chunk g of this step -- byte 256*(j/4) + 64*(step%4) + 16*g +
+//     4*(j%4) of the band's 1 KiB tile -- which is exactly the B operand of
+//     v_mfma_i32_16x16x64_i8 for that band (16 K of one column);
 //     v_perm_b32 turns the 2-bit codes into signed int8 weights (code 0, the
 //     padding, becomes 0) after each shift-and-mask of [W2A8] §5.2;
 //   * the A operand (16 rows m x 64 K) is read straight from the int8
@@ -49,9 +50,11 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
     __shared__ int red[MT * 16][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int band = blockIdx.x;
+    const int col = blockIdx.x;                      // 64 output rows = 4 bands
+    const int nbands = (N + kTileRows - 1) / kTileRows;
     const int m0 = blockIdx.y * 64;
-    const int S = (K + kTileK - 1) / kTileK;
+    const int S256 = (K + kTileK - 1) / kTileK;      // 1 KiB tiles per band
+    const int S = (K + 63) / 64;                     // 64-K MFMA steps
     const int s0 = (S * wave) / kMfmaWaves;
     const int s1 = (S * (wave + 1)) / kMfmaWaves;
     const int j = lane & 15;
@@ -65,16 +68,19 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t) c[mt][t] = v4i{0, 0, 0, 0};
 
-    const uint32_t* band_words =
-        reinterpret_cast<const uint32_t*>(packed + static_cast<size_t>(band) * S * kTileBytes);
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(packed);
+    size_t band_base[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        band_base[t] = static_cast<size_t>(min(4 * col + t, nbands - 1)) * S256 * (kTileBytes / 4);
+    const int lane_word = 64 * (j >> 2) + 4 * g + (j & 3);
     for (int st = s0; st < s1; ++st) {
-        const uint32_t* tile = band_words + static_cast<size_t>(st) * (kTileBytes / 4);
+        const size_t step_word = static_cast<size_t>(st >> 2) * (kTileBytes / 4) + 16 * (st & 3) + lane_word;
         uint32_t bw[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            bw[t] = __builtin_nontemporal_load(tile + 64 * t + 16 * (j >> 2) + 4 * g + (j & 3));
+        for (int t = 0; t < 4; ++t) bw[t] = __builtin_nontemporal_load(words + band_base[t] + step_word);
         v4i a[MT];
-        const int k = st * kTileK + 16 * g;
+        const int k = st * 64 + 16 * g;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = m0 + 16 * mt + j;
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
         const int ml = i >> 6;
         const int nl = i & 63;
         const int m = m0 + ml;
-        const int n = band * 64 + nl;
+        const int n = col * 64 + nl;
         if (m < M && n < N) {
             const int32_t total = red[ml][nl];
             const size_t o = static_cast<size_t>(m) * N + n;
@@ -121,8 +127,7 @@ template <int MT>
 hipError_t launch_mt(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,
                      int ws_num, uint16_t* y, int32_t* acc, int M, int N, int K,
                      hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>((N + kTileRows - 1) / kTileRows),
-                    static_cast<unsigned>((M + 63) / 64));
+    const dim3 grid(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((M + 63) / 64));
     gemm_mfma_kernel<MT><<<grid, kMfmaThreads, 0, stream>>>(xq, packed, s, ws, ws_num, y, acc, M,
                                                              N, K);
     return hipGetLastError();

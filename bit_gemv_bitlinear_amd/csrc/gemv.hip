@@ -7,29 +7,32 @@
 // (per-token activation quantisation, fused here for bf16 input).
 //
 // Mapping (this library's design; the page's sm_80 kernel is prior art):
-//   * one workgroup per band of 64 output rows; its W wavefronts split the
-//     band's S K-steps (64 K = one 1 KiB tile each), P consecutive steps per
-//     wavefront, W and P picked per shape so that W*P covers S with the least
-//     waste and the steps spread evenly over the 4 SIMDs;
+//   * a band is 16 output rows; a workgroup takes B = 1, 2 or 4 consecutive
+//     bands (more for wide matrices, so that each activation staging serves
+//     more rows; fewer for narrow ones, so that there are enough workgroups);
+//     the Wb wavefronts of a band split its S K-steps (256 K = one 1 KiB
+//     tile each), P consecutive steps per wavefront, (B, Wb, P) picked per
+//     shape by gemv_shape();
 //   * a wavefront's load of a tile is one coalesced 16-byte-per-lane load of
-//     1 KiB; lane l's slot holds rows 4*(l/4) .. +3 of K chunk l%4, so each
+//     1 KiB; lane l's slot holds rows 4*(l/16) .. +3 of K chunk l%16, so each
 //     lane needs one 16-byte run of activations per step;
 //   * every weight load of the wavefront is issued up front (P is a template
 //     argument, so the loads are unconditional and the compiler counts them
-//     exactly), before the activations are staged;
+//     exactly), after the activation row and the lane's weight scale;
 //   * the activation row is staged once per workgroup in LDS (zero-padded to
-//     W*P steps; steps past the band's end re-read its last tile and meet zero
-//     activations), read back as one 16-byte LDS load per step;
+//     Wb*P steps; steps past the band's end re-read its last tile and meet
+//     zero activations), read back as one 16-byte LDS load per step;
 //   * decoding keeps the unsigned codes c = w + 2 and never shifts them into
 //     place: field i of a word is masked in place (factor 4^i, i < 3) and
 //     dotted with activation word i into one of three accumulators; field 3
 //     is shifted down once.  acc = a1 + a4/4 + a16/16 - 2 * sum(x), the last
 //     term removing the +2 offset (padding code 0 contributes nothing);
-//   * the 4 lanes sharing a K step exchange partial sums with DPP so that
-//     lane r ends with row r; the W wavefronts' sums are added through LDS;
-//     the epilogue multiplies by a precomputed fp64 1/s and rounds once to
+//   * the 16 lanes sharing four rows add their partial sums with DPP row
+//     operations; the Wb wavefronts of a band are added through LDS;
+//   * the epilogue multiplies by a precomputed fp64 1/s and rounds once to
 //     bf16, dividing only when the product lies next to a rounding boundary
 //     (so the result is that of the exact fp64 division).
+#include <algorithm>
 #include <array>
 #include <utility>
 
@@ -74,28 +77,34 @@ __device__ __forceinline__ void load_steps(const v4u* __restrict__ tiles, int s0
     }
 }
 
-// DPP lane exchange inside groups of 4 lanes.
+// DPP exchanges inside a row of 16 lanes.
 template <int CTRL>
-__device__ __forceinline__ int quad_swap(int v) {
+__device__ __forceinline__ int dpp_move(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 constexpr int kQuadXor1 = 0xB1;   // quad_perm(1, 0, 3, 2)
 constexpr int kQuadXor2 = 0x4E;   // quad_perm(2, 3, 0, 1)
+constexpr int kRowRor4 = 0x124;   // lane i <- lane (i + 4) % 16 inside each 16 lanes
+constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) % 16
 
-// Lanes 4g..4g+3 each hold partial sums of rows 4g..4g+3 (over their own K
-// chunks); afterwards lane 4g + c holds the full sum of row 4g + c.
-__device__ __forceinline__ int quad_reduce_scatter(const int (&v)[4], int lane) {
+// Each lane holds partial sums of the four rows of its 16-lane group (over
+// its own K chunk).  Afterwards lane l holds the full sum, over the 16 lanes,
+// of row l % 4 of the group: a reduce-scatter inside each quad, then a sum
+// over the four quads by rotations that keep l % 4.
+__device__ __forceinline__ int row_group_reduce(const int (&v)[4], int lane) {
     const bool b = (lane >> 1) & 1;
     const int send0 = b ? v[0] : v[2];
     const int send1 = b ? v[1] : v[3];
     int keep0 = b ? v[2] : v[0];
     int keep1 = b ? v[3] : v[1];
-    keep0 += quad_swap<kQuadXor2>(send0);
-    keep1 += quad_swap<kQuadXor2>(send1);
+    keep0 += dpp_move<kQuadXor2>(send0);
+    keep1 += dpp_move<kQuadXor2>(send1);
     const bool a = lane & 1;
     const int send = a ? keep0 : keep1;
     int keep = a ? keep1 : keep0;
-    keep += quad_swap<kQuadXor1>(send);
+    keep += dpp_move<kQuadXor1>(send);     // row 2b + a = lane % 4, summed over the quad
+    keep += dpp_move<kRowRor4>(keep);
+    keep += dpp_move<kRowRor8>(keep);       // summed over the four quads
     return keep;
 }
 
@@ -126,7 +135,8 @@ __device__ __forceinline__ int sum_i8x4(uint32_t d, int acc) {
     return dot4(static_cast<int>(d), 0x01010101, acc);
 }
 
-// seg = N / ws_num: rows per weight scale.
+// seg = N / ws_num: rows per weight scale.  B bands per workgroup, 2^lw
+// wavefronts per band (blockDim.x = 64 * B * 2^lw), P K-steps per wavefront.
 // FUSED = false: xin is int8 activations with scale s_in[0].
 // FUSED = true:  xin is bf16; the workgroup quantises it (per-token absmax,
 //                [W2A8] §六 item 3); workgroup 0 writes q_out / s_out if given.
@@ -135,27 +145,29 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     const void* __restrict__ xin, const v4u* __restrict__ packed, const float* __restrict__ s_in,
     const uint16_t* __restrict__ ws, int seg, uint16_t* __restrict__ y,
     int32_t* __restrict__ acc, int8_t* __restrict__ q_out, float* __restrict__ s_out, int N,
-    int K) {
-    extern __shared__ int4 act[];   // W*P*4 16-byte chunks: the int8 row, zero-padded
+    int K, int B, int lw) {
+    extern __shared__ int4 act[];   // Wb*P*16 16-byte chunks: the int8 row, zero-padded
     __shared__ int part_sh[kMaxWaves][64];
     __shared__ int xsum_sh[kMaxWaves];
     __shared__ float amax_sh[kMaxWaves];
-    const int nthreads = blockDim.x;
-    const int W = nthreads >> 6;
+    const int Wb = 1 << lw;
+    const int W = B << lw;
+    const int nthreads = W * 64;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int band = blockIdx.x;
+    const int nbands = (N + kTileRows - 1) / kTileRows;
+    const int band = min(static_cast<int>(blockIdx.x) * B + (wave >> lw), nbands - 1);
     const int S = (K + kTileK - 1) / kTileK;
-    const int s0 = wave * P;
+    const int s0 = (wave & (Wb - 1)) * P;
     const int n16 = K >> 4;        // 16-byte chunks of int8 activations
-    const int padded16 = W * P * 4;
+    const int padded16 = Wb * P * 16;
 
-    // 1. The activation row and this lane's weight scale first (so that
-    //    waiting for them does not wait for the weights), then every weight
-    //    load of this wavefront.
-    const int n = band * 64 + lane;
-    const uint16_t wsb = ws[min(n, N - 1) / seg];   // unconditional: no branch, no early wait
+    // 1. The activation row and the weight scale of this thread's output row
+    //    first (so that waiting for them does not wait for the weights), then
+    //    every weight load of this wavefront.
+    const int n_out = static_cast<int>(blockIdx.x) * B * kTileRows + tid;   // tid < 16*B writes
+    const uint16_t wsb = ws[min(n_out, N - 1) / seg];   // unconditional: no branch, no early wait
     uint4 xv[kCached];
     const int n_in = FUSED ? (K >> 3) : n16;   // 16-byte input chunks
     const uint4* x16 = reinterpret_cast<const uint4*>(xin);
@@ -200,7 +212,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
         for (int i = 1; i < W; ++i) amax = fmaxf(amax, amax_sh[i]);
         sm = 127.0f / fmaxf(amax, 1e-5f);
         uint2* act8 = reinterpret_cast<uint2*>(act);
-        const bool write_q = (band == 0) && (q_out != nullptr);
+        const bool write_q = (blockIdx.x == 0) && (q_out != nullptr);
 #pragma unroll
         for (int c = 0; c < kCached; ++c) {
             const int idx = tid + c * nthreads;
@@ -217,7 +229,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
             xs = sum_i8x4(o.x, sum_i8x4(o.y, xs));
             if (write_q) reinterpret_cast<uint2*>(q_out)[idx] = o;
         }
-        if (band == 0 && s_out != nullptr && tid == 0) s_out[0] = sm;
+        if (blockIdx.x == 0 && s_out != nullptr && tid == 0) s_out[0] = sm;
     }
     for (int i = n16 + tid; i < padded16; i += nthreads) act[i] = make_int4(0, 0, 0, 0);
     // 1/s for the epilogue, computed here while the weights are in flight;
@@ -228,40 +240,47 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     xs = wave_sum(xs);
     if (lane == 0) xsum_sh[wave] = xs;
     __syncthreads();
+    // The code offset correction, -2 * sum(x), summed here while the weights
+    // are still in flight rather than after the last barrier.
+    int offset = 0;
+    for (int i = 0; i < W; ++i) offset -= 2 * xsum_sh[i];
 
     // 3. P steps of 4 rows x 16 K per lane.
     RowAcc r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.a1[i] = r.a4[i] = r.a16[i] = 0;
-    const int kc = lane & 3;
+    const int kc = lane & 15;
 #pragma unroll
-    for (int u = 0; u < P; ++u) dot_slot(w[u], act[(s0 + u) * 4 + kc], r);
+    for (int u = 0; u < P; ++u) dot_slot(w[u], act[(s0 + u) * 16 + kc], r);
     int v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = r.a1[i] + (r.a4[i] >> 2) + (r.a16[i] >> 4);   // exact
-    part_sh[wave][lane] = quad_reduce_scatter(v, lane);
+    // lane l now holds row 4*(l/16) + l%4 of its band (replicated over l/4 % 4)
+    part_sh[wave][lane] = row_group_reduce(v, lane);
     __syncthreads();
 
-    // 4. Wavefront 0: add the W partial sums of row `lane`, remove the code
-    //    offset, epilogue.
+    // 4. Wavefront 0, lane l < 16*B: row l % 16 of band l / 16 -- add the
+    //    Wb wavefronts' sums, remove the code offset, epilogue.
     if (wave == 0) {
-        int total = 0, xsum = 0;
-        for (int i = 0; i < W; ++i) {
-            total += part_sh[i][lane];
-            xsum += xsum_sh[i];
-        }
-        total -= 2 * xsum;
-        if (n < N) {
-            y[n] = epilogue_bf16_fast(total, bf16_to_float(wsb), sm, inv_s);
-            if (acc) acc[n] = total;
+        const int bw = lane >> 4;
+        const int rw = lane & 15;
+        const int slot = 16 * (rw >> 2) + (rw & 3);
+        const int first = min(bw, B - 1) << lw;   // in range for every lane
+        int total = offset;
+        for (int j = 0; j < Wb; ++j) total += part_sh[first + j][slot];
+        if (bw < B && n_out < N) {
+            y[n_out] = epilogue_bf16_fast(total, bf16_to_float(wsb), sm, inv_s);
+            if (acc) acc[n_out] = total;
         }
     }
 }
 
 constexpr int kMaxSteps = 20;
+constexpr int kMinGroups = 200;     // workgroups wanted in flight (256 CUs)
+constexpr int kTargetSteps = 9;     // K steps per wavefront aimed at
 
 using GemvFn = void (*)(const void*, const v4u*, const float*, const uint16_t*, int, uint16_t*,
-                        int32_t*, int8_t*, float*, int, int);
+                        int32_t*, int8_t*, float*, int, int, int, int);
 
 template <bool FUSED, int... Ps>
 constexpr std::array<GemvFn, sizeof...(Ps)> kernel_table(std::integer_sequence<int, Ps...>) {
@@ -276,37 +295,35 @@ const std::array<GemvFn, kMaxSteps> kBf16Kernels =
 hipError_t launch(bool fused, const void* x, const uint8_t* packed, const float* s,
                   const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int8_t* q_out,
                   float* s_out, int N, int K, hipStream_t stream) {
-    const GemvShape g = gemv_shape(K);
+    const GemvShape g = gemv_shape(N, K);
     if (g.waves == 0) return hipErrorInvalidValue;
-    const unsigned bands = static_cast<unsigned>((N + kTileRows - 1) / kTileRows);
-    const size_t lds = static_cast<size_t>(g.waves) * g.steps * kTileK;
+    const int nbands = (N + kTileRows - 1) / kTileRows;
+    const unsigned groups = static_cast<unsigned>((nbands + g.bands - 1) / g.bands);
+    const int wb = g.waves / g.bands;
+    int lw = 0;
+    while ((1 << lw) < wb) ++lw;
+    const size_t lds = static_cast<size_t>(wb) * g.steps * kTileK;
     const GemvFn fn = fused ? kBf16Kernels[g.steps - 1] : kI8Kernels[g.steps - 1];
-    fn<<<bands, g.waves * 64, lds, stream>>>(x, reinterpret_cast<const v4u*>(packed), s, ws,
-                                            N / ws_num, y, acc, q_out, s_out, N, K);
+    fn<<<groups, g.waves * 64, lds, stream>>>(x, reinterpret_cast<const v4u*>(packed), s, ws,
+                                             N / ws_num, y, acc, q_out, s_out, N, K, g.bands, lw);
     return hipGetLastError();
 }
 
 }  // namespace
 
-GemvShape gemv_shape(int K) {
-    // W wavefronts x P steps covering S steps: minimise the busiest SIMD's
-    // step count (ceil(W/4) * P), then the wasted steps, then prefer more
-    // wavefronts.
+GemvShape gemv_shape(int N, int K) {
     const int S = (K + kTileK - 1) / kTileK;
-    GemvShape best{0, 0};
-    int best_load = 1 << 30, best_waste = 1 << 30;
-    for (int W = kMaxWaves; W >= 1; --W) {
-        const int P = (S + W - 1) / W;
-        if (P > kMaxSteps) continue;
-        const int load = ((W + 3) / 4) * P;
-        const int waste = W * P - S;
-        if (load < best_load || (load == best_load && waste < best_waste)) {
-            best = GemvShape{W, P};
-            best_load = load;
-            best_waste = waste;
-        }
-    }
-    return best;
+    const int nbands = (N + kTileRows - 1) / kTileRows;
+    // Wavefronts per band: the smallest power of two (the kernel splits by
+    // shifts) that leaves at most kTargetSteps steps per wavefront.
+    int Wb = 1;
+    while (Wb < kMaxWaves && (S + Wb - 1) / Wb > kTargetSteps) Wb <<= 1;
+    const int P = (S + Wb - 1) / Wb;
+    if (P > kMaxSteps) return GemvShape{0, 0, 0};
+    // Bands per workgroup: as many as keep >= kMinGroups workgroups in flight.
+    int B = 4;
+    while (B > 1 && (nbands / B < kMinGroups || B * Wb > kMaxWaves)) B >>= 1;
+    return GemvShape{B * Wb, P, B};
 }
 
 hipError_t launch_gemv_i8(const int8_t* xq, const uint8_t* packed, const float* s,

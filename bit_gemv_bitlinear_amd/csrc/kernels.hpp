@@ -18,15 +18,17 @@ int64_t pack_host(const int8_t* w, uint8_t* packed, int N, int K);
 hipError_t launch_quant(const void* x, int x_is_bf16, int8_t* q, float* s, int M, int K,
                         hipStream_t stream);
 
-// M == 1 GEMV geometry: `waves` wavefronts per workgroup, `steps` K steps
-// (64 K each) per wavefront; waves == 0 when K is beyond the GEMV kernels
-// (K > kGemvMaxK), which then leave M == 1 to the MFMA kernel.
+// M == 1 GEMV geometry: `waves` wavefronts per workgroup covering `bands`
+// 16-row bands, `steps` K steps (256 K each) per wavefront; waves == 0 when
+// K is beyond the GEMV kernels (K > kGemvMaxK), which then leave M == 1 to
+// the MFMA kernel.
 struct GemvShape {
     int waves;
     int steps;
+    int bands;
 };
-constexpr int kGemvMaxK = 64 * 16 * 20;
-GemvShape gemv_shape(int K);
+constexpr int kGemvMaxK = 61440;   // LDS copy of the row <= 60 KiB
+GemvShape gemv_shape(int N, int K);
 
 // M == 1, int8 activations; K <= kGemvMaxK.
 hipError_t launch_gemv_i8(const int8_t* xq, const uint8_t* packed, const float* s,

@@ -3,7 +3,7 @@
 // Source page: "BitNet GPU 推理框架：从零构建 W2A8 的 2-bit 大模型 CUDA GEMV 内核"
 // (blog.gitcode.com), §5.2: each weight w in {-1, 0, 1} becomes the code
 // w + 2, and the 16 codes of a 32-bit word are interleaved so that element e
-// sits at bit 8*(e%4) + 2*(e/4).  The tiling around the words (64 rows x 64 K
+// sits at bit 8*(e%4) + 2*(e/4).  The tiling around the words (16 rows x 256 K
 // per 1 KiB tile, one 16-byte slot per wavefront lane) is this library's
 // own (a 16-byte slot holds four rows of one 16-wide K chunk, so a lane's
 // 16-byte load needs a single 16-byte run of activations); it is spelled out
@@ -27,9 +27,9 @@ __host__ __device__ inline uint32_t ternary_code(int w) {
 __host__ __device__ inline int bit_of(int e) { return 8 * (e & 3) + 2 * (e >> 2); }
 
 // One thread per packed 32-bit word.  Word u of tile t is word i = u % 4 of
-// slot q = u / 4; it holds k = 64*(t % S) + 16*(q % 4) + e for e = 0..15 of
-// row n = 64*(t / S) + 4*(q / 4) + i.  VEC: the 16 source bytes are read as
-// one 16-byte load (w 16-byte aligned, K % 16 == 0).
+// slot q = u / 4; it holds k = 256*(t % S) + 16*(q % 16) + e for e = 0..15
+// of row n = 16*(t / S) + 4*(q / 16) + i.  VEC: the 16 source bytes are read
+// as one 16-byte load (w 16-byte aligned, K % 16 == 0).
 template <bool VEC>
 __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ w,
                                                    uint32_t* __restrict__ packed, int N, int K,
@@ -40,8 +40,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ w,
     const size_t t = i >> 8;
     const int u = static_cast<int>(i & 255);
     const int q = u >> 2;
-    const int n = static_cast<int>(t / S) * kTileRows + 4 * (q >> 2) + (u & 3);
-    const int k0 = static_cast<int>(t % S) * kTileK + 16 * (q & 3);
+    const int n = static_cast<int>(t / S) * kTileRows + 4 * (q >> 4) + (u & 3);
+    const int k0 = static_cast<int>(t % S) * kTileK + 16 * (q & 15);
     uint32_t word = 0;
     int bad = 0;
     if (n < N && k0 < K) {
@@ -94,8 +94,8 @@ int64_t pack_host(const int8_t* w, uint8_t* packed, int N, int K) {
         const size_t t = i >> 8;
         const int u = static_cast<int>(i & 255);
         const int q = u >> 2;
-        const int n = static_cast<int>(t / S) * kTileRows + 4 * (q >> 2) + (u & 3);
-        const int k0 = static_cast<int>(t % S) * kTileK + 16 * (q & 3);
+        const int n = static_cast<int>(t / S) * kTileRows + 4 * (q >> 4) + (u & 3);
+        const int k0 = static_cast<int>(t % S) * kTileK + 16 * (q & 15);
         uint32_t word = 0;
         if (n < N) {
             for (int e = 0; e < 16 && k0 + e < K; ++e) {

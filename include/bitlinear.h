@@ -39,17 +39,17 @@
  *     These are not checked on the device; other values give undefined
  *     results (never out-of-bounds accesses).
  *
- * Packed weight layout ("64x64 tiles")
+ * Packed weight layout ("16x256 tiles")
  *   The weight w[n][k] of an N x K matrix (row n produces output n) is the
  *   2-bit code w + 2 ({-1,0,1} -> {1,2,3}, [W2A8] §5.2).  Code 0 marks
- *   padding.  With S = ceil(K/64) steps and ceil(N/64) bands:
- *     tile  t = (n / 64) * S + k / 64                    1024 bytes per tile
- *     slot  q = 4 * ((n % 64) / 4) + (k % 64) / 16       16 bytes per slot
+ *   padding.  With S = ceil(K/256) steps and ceil(N/16) bands:
+ *     tile  t = (n / 16) * S + k / 256                   1024 bytes per tile
+ *     slot  q = 16 * ((n % 16) / 4) + (k % 256) / 16     16 bytes per slot
  *     byte  t*1024 + 16*q + 4*(n % 4) + (k % 16) % 4
  *     bits  2*((k % 16) / 4) and the next one
- *   i.e. a tile is 64 rows x 64 K; slot q holds four 32-bit words, rows
- *   4*(q/4) .. +3 of the 16-wide K chunk q%4; inside a word element e sits at
- *   bit 8*(e%4) + 2*(e/4): the page's interleave 0,4,8,12,1,5,... ([W2A8]
+ *   i.e. a tile is 16 rows x 256 K; slot q holds four 32-bit words, rows
+ *   4*(q/16) .. +3 of the 16-wide K chunk q%16; inside a word element e sits
+ *   at bit 8*(e%4) + 2*(e/4): the page's interleave 0,4,8,12,1,5,... ([W2A8]
  *   §5.2), so (word >> 2i) & 0x03030303 holds elements 4i..4i+3 as bytes.
  *   Lane l of a 64-wide wavefront reads slot l with one 16-byte load (a
  *   wavefront's load of a tile is 1 KiB contiguous) and needs one 16-byte
@@ -83,13 +83,14 @@ int bl_abi_version(void);
 
 /*
  * Size in bytes of the packed buffer for an N x K matrix:
- * ceil(N/64) * ceil(K/64) * 1024 (exactly N*K/4 when 64 divides N and K).
+ * ceil(N/16) * ceil(K/256) * 1024 (exactly N*K/4 when 16 divides N and 256
+ * divides K).
  * Returns 0 for N < 1 or K < 1.
  */
 size_t bl_packed_bytes(int N, int K);
 
 /*
- * pack_ternary_weights -- pack a ternary matrix into the 64x64-tile layout
+ * pack_ternary_weights -- pack a ternary matrix into the 16x256-tile layout
  * ([W2A8] §5.1-5.2: code w + 2, four codes per byte, interleaved words).
  *   w          device, int8, N x K row-major (row n = output n)
  *   packed     device, bl_packed_bytes(N, K) bytes, written in full
@@ -131,7 +132,7 @@ int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int 
  *   acc[m][n] = sum_k xq[m][k] * w[n][k]                       exact int32
  *   y[m][n]   = bf16_rne( (double)acc[m][n] * ws[n / (N / ws_num)] / s[m] )
  *   xq       device, int8, M x K row-major
- *   packed   device, bl_packed_bytes(N, K) bytes, 64x64-tile layout
+ *   packed   device, bl_packed_bytes(N, K) bytes, 16x256-tile layout
  *   s        device, fp32, M activation scales (127 / amax of each row)
  *   ws       device, bf16, ws_num weight scales, one per equal N-segment
  *   ws_num   1 <= ws_num <= 64 and N % ws_num == 0
@@ -139,9 +140,10 @@ int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int 
  *   acc      device, int32, M x N row-major, or NULL (not written)
  * The activation scale divides: s = 127/amax quantised the activations, so
  * y approximates x . w^T * ws.
- * M == 1 with K <= 20480 runs the GEMV kernel (one workgroup per 64 output
- * rows, v_dot4 on masked codes); M >= 2, or K > 20480, runs the int8 MFMA
- * kernel (v_mfma_i32_16x16x64_i8), 64 rows of M per workgroup column.
+ * M == 1 with K <= 61440 runs the GEMV kernel (workgroups of 1, 2 or 4
+ * 16-row bands, v_dot4 on masked codes); M >= 2, or K > 61440, runs the
+ * int8 MFMA kernel (v_mfma_i32_16x16x64_i8), 64 rows of M per workgroup
+ * column.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_ARG, BL_ERR_HIP.
  */
 int bitlinear_i8xi2(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,
@@ -157,8 +159,8 @@ int bitlinear_i8xi2(const int8_t* xq, const uint8_t* packed, const float* s, con
  *   q_out    device, int8, M x K, or NULL: the quantised activations
  *   s_out    device, fp32, M, or NULL: the activation scales
  *   acc      device, int32, M x N, or NULL
- * M == 1 and K <= 20480: one fused kernel (each workgroup quantises the row
- * into LDS).  M >= 2 or K > 20480: q_out and s_out are required (they are
+ * M == 1 and K <= 61440: one fused kernel (each workgroup quantises the row
+ * into LDS).  M >= 2 or K > 61440: q_out and s_out are required (they are
  * the staging buffers of a quantise kernel followed by the layer kernel);
  * BL_ERR_NULL otherwise.
  * Errors: as bitlinear_i8xi2.
@@ -187,7 +189,7 @@ typedef struct bl_gemv_desc {
 typedef struct bl_graph bl_graph;
 
 /*
- * Capture the n calls (1 <= n <= 65536; every descriptor K <= 20480) on an
+ * Capture the n calls (1 <= n <= 65536; every descriptor K <= 61440) on an
  * internal stream and instantiate them.  The descriptors are validated first; the pointers they
  * hold are baked into the graph and must stay valid while it exists.
  * *out receives the graph (NULL on error).

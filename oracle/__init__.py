@@ -123,7 +123,7 @@ def quant_absmax_i8(x: np.ndarray, bf16: bool = False):
 # --------------------------------------------------------------------------
 
 def packed_bytes(N: int, K: int) -> int:
-    """Bytes of the 64x64-tiled packed layout: ceil(N/64)*ceil(K/64)*1024."""
+    """Bytes of the tiled packed layout: ceil(N/16)*ceil(K/256)*1024."""
     return int(_load().oracle_packed_bytes(N, K))
 
 

@@ -18,7 +18,7 @@
  *                    byte, the 16 codes of a 32-bit word interleaved so that
  *                    shift 2i + mask 0x03030303 yields elements 4i..4i+3
  *                                                                  [W2A8] §5.2
- *                    (the 64-row x 64-K tiling is this project's own layout;
+ *                    (the 16-row x 256-K tiling is this project's own layout;
  *                    its bit-level definition is restated at unpack_r64)
  *   gemm_i32         int32 dot products of int8 activations and ternary
  *                    weights, exactly the int32 matmul the page's test uses
@@ -181,34 +181,45 @@ int oracle_quant_absmax_i8_bf16(const uint16_t* x, int M, int K, int8_t* q, floa
 /* ---------------------------------------------------------------------- */
 
 /*
- * Packed size of an N x K ternary matrix in the 64x64-tiled layout:
- * ceil(N/64) * ceil(K/64) tiles of 1024 bytes each.
+ * Packed size of an N x K ternary matrix in the tiled layout: ceil(N/16) *
+ * ceil(K/256) tiles of 1024 bytes each.
  */
 size_t oracle_packed_bytes(int N, int K)
 {
     if (N <= 0 || K <= 0)
         return 0;
-    size_t bands = ((size_t)N + 63) / 64;
-    size_t steps = ((size_t)K + 63) / 64;
+    size_t bands = ((size_t)N + 15) / 16;
+    size_t steps = ((size_t)K + 255) / 256;
     return bands * steps * 1024;
+}
+
+/* Byte offset and bit position of element (n, k) in the tiled layout. */
+static size_t layout_byte(size_t n, size_t k, size_t steps, int *bit)
+{
+    size_t t = (n / 16) * steps + k / 256;
+    size_t q = 16 * ((n % 16) / 4) + (k % 256) / 16;
+    size_t i = n % 4;
+    size_t e = k % 16;
+    *bit = (int)(2 * (e / 4));
+    return t * 1024 + 16 * q + 4 * i + e % 4;
 }
 
 /*
  * Layout, stated at the level of single bits.  The weight w[n][k] of an
  * N x K matrix (row n = output n) is stored as the 2-bit code w + 2
  * ({-1,0,1} -> {1,2,3}, as on [W2A8] §5.2); the code lives in
- *   tile      t = (n / 64) * ceil(K/64) + (k / 64)       (1024 bytes each)
- *   slot      q = 4 * ((n % 64) / 4) + (k % 64) / 16     (16 bytes each)
+ *   tile      t = (n / 16) * ceil(K/256) + (k / 256)     (1024 bytes each)
+ *   slot      q = 16 * ((n % 16) / 4) + (k % 256) / 16   (16 bytes each)
  *   word      i = n % 4                                  (4 bytes each, little endian)
  *   element   e = k % 16
  *   byte      t*1024 + 16*q + 4*i + (e % 4)
  *   bits      2*(e / 4) .. 2*(e / 4) + 1 of that byte
- * so a 16-byte slot holds four rows (4*((n%64)/4) .. +3) of one 16-wide K
- * chunk, and inside each 32-bit word element e sits at bit 8*(e%4) + 2*(e/4):
- * the word holds its 16 elements in the page's interleaved order
- * 0,4,8,12,1,5,9,13,2,6,10,14,3,7,11,15 ([W2A8] §5.2).
- * Positions with n >= N or k >= K (padding of the last tile row/column)
- * hold code 0.  Code 0 at a real position is an error.
+ * so a tile is 16 rows x 256 K, a 16-byte slot holds four rows
+ * (4*((n%16)/4) .. +3) of one 16-wide K chunk, and inside each 32-bit word
+ * element e sits at bit 8*(e%4) + 2*(e/4): the word holds its 16 elements
+ * in the page's interleaved order 0,4,8,12,1,5,9,13,2,6,10,14,3,7,11,15
+ * ([W2A8] §5.2).  Positions with n >= N or k >= K (padding of the last
+ * tile row/column) hold code 0.  Code 0 at a real position is an error.
  *
  * Returns OR_OK, OR_ERR_CODE (and *bad = flat index n*K+k of the first bad
  * code) or OR_ERR_PAD (and *bad = byte offset of the first bad padding byte).
@@ -217,17 +228,13 @@ int oracle_unpack_r64(const uint8_t* packed, int N, int K, int8_t* w, int64_t* b
 {
     if (!packed || !w || N <= 0 || K <= 0)
         return OR_ERR_ARG;
-    size_t steps = ((size_t)K + 63) / 64;
-    size_t bands = ((size_t)N + 63) / 64;
+    size_t steps = ((size_t)K + 255) / 256;
+    size_t bands = ((size_t)N + 15) / 16;
     /* every real position */
     for (int n = 0; n < N; ++n) {
         for (int k = 0; k < K; ++k) {
-            size_t t = (size_t)(n / 64) * steps + (size_t)(k / 64);
-            size_t q = 4 * (size_t)((n % 64) / 4) + (size_t)((k % 64) / 16);
-            size_t i = (size_t)(n % 4);
-            int e = k % 16;
-            size_t byte = t * 1024 + 16 * q + 4 * i + (size_t)(e % 4);
-            int bit = 2 * (e / 4);
+            int bit;
+            size_t byte = layout_byte((size_t)n, (size_t)k, steps, &bit);
             int code = (packed[byte] >> bit) & 3;
             if (code == 0) {
                 if (bad)
@@ -238,25 +245,16 @@ int oracle_unpack_r64(const uint8_t* packed, int N, int K, int8_t* w, int64_t* b
         }
     }
     /* every padding position must be code 0 */
-    for (size_t band = 0; band < bands; ++band) {
-        for (size_t st = 0; st < steps; ++st) {
-            for (int r = 0; r < 64; ++r) {
-                for (int kk = 0; kk < 64; ++kk) {
-                    size_t n = band * 64 + (size_t)r;
-                    size_t k = st * 64 + (size_t)kk;
-                    if (n < (size_t)N && k < (size_t)K)
-                        continue;
-                    size_t t = band * steps + st;
-                    size_t q = 4 * (size_t)(r / 4) + (size_t)(kk / 16);
-                    int e = kk % 16;
-                    size_t byte = t * 1024 + 16 * q + 4 * (size_t)(r % 4) + (size_t)(e % 4);
-                    int code = (packed[byte] >> (2 * (e / 4))) & 3;
-                    if (code != 0) {
-                        if (bad)
-                            *bad = (int64_t)byte;
-                        return OR_ERR_PAD;
-                    }
-                }
+    for (size_t n = 0; n < bands * 16; ++n) {
+        for (size_t k = 0; k < steps * 256; ++k) {
+            if (n < (size_t)N && k < (size_t)K)
+                continue;
+            int bit;
+            size_t byte = layout_byte(n, k, steps, &bit);
+            if (((packed[byte] >> bit) & 3) != 0) {
+                if (bad)
+                    *bad = (int64_t)byte;
+                return OR_ERR_PAD;
             }
         }
     }

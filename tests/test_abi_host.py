@@ -46,7 +46,8 @@ def test_packed_bytes_matches_oracle(N, K):
     assert bl.bl_packed_bytes(N, K) == (oracle.packed_bytes(N, K) if N > 0 and K > 0 else 0)
 
 
-@pytest.mark.parametrize("N,K", [(64, 64), (128, 2560), (70, 80), (1, 16), (130, 6912), (3, 200)])
+@pytest.mark.parametrize("N,K", [(16, 256), (128, 2560), (70, 80), (1, 16), (130, 6912), (3, 200),
+                                 (17, 300)])
 def test_host_packer_round_trips_through_oracle_unpack(N, K):
     g = np.random.Generator(np.random.PCG64(N * 100003 + K))
     w = g.integers(-1, 2, size=(N, K), dtype=np.int8)
@@ -56,13 +57,13 @@ def test_host_packer_round_trips_through_oracle_unpack(N, K):
 
 
 def test_host_packer_counts_invalid_entries():
-    w = np.zeros((64, 64), dtype=np.int8)
+    w = np.zeros((16, 256), dtype=np.int8)
     w[3, 4] = 2
     w[5, 6] = -7
     packed, bad = bl.bl_pack_ternary_host(w)
     assert bad == 2
     with pytest.raises(oracle.OracleError, match="code 0"):
-        oracle.unpack_r64(packed, 64, 64)
+        oracle.unpack_r64(packed, 16, 256)
 
 
 # Argument validation.  Non-null dummy addresses are fine: every call below
@@ -104,7 +105,7 @@ def test_bitlinear_bf16_errors():
     assert _bf(x=None) == bl.BL_ERR_NULL
     assert _bf(M=2) == bl.BL_ERR_NULL                    # M > 1 needs the staging buffers
     assert _bf(M=2, q=A) == bl.BL_ERR_NULL
-    assert _bf(K=20480 + 16) == bl.BL_ERR_NULL           # beyond the fused K limit
+    assert _bf(K=61440 + 16) == bl.BL_ERR_NULL           # beyond the fused K limit
     assert _bf(K=40) == bl.BL_ERR_SHAPE
     assert _bf(ws_num=2, N=65) == bl.BL_ERR_ARG
     assert _bf(x=A + 8) == bl.BL_ERR_ALIGN

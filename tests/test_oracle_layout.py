@@ -5,7 +5,7 @@ The page ("BitNet GPU 推理框架：从零构建 W2A8 的 2-bit 大模型 CUDA 
 decode constants and the 16x32 permutation; tests/golden holds them.  Checks:
   * the page's own chain (+2, permute, compress, interleave) round-trips through
     the page's decode, and its printed pattern/shift table agree with each other;
-  * hand-worked bytes of the 64x64-tiled layout decode to the right (n, k);
+  * hand-worked bytes of the 16x256-tiled layout decode to the right (n, k);
   * every 32-bit word of the tiled layout, decoded the page's way (shift, mask,
     subtract 2), gives the same 16 weights as the oracle's bit-by-bit unpack;
   * code 0 at a real position and non-zero padding are reported.
@@ -82,41 +82,41 @@ def test_hand_worked_tiled_bytes():
         n, k, v, off, byte = int(n), int(k), int(v), int(off), int(byte, 16)
         p = _all_zero_tile()
         p[off] = byte
-        w = oracle.unpack_r64(p, 64, 64)
-        expect = np.zeros((64, 64), dtype=np.int8)
+        w = oracle.unpack_r64(p, 16, 256)
+        expect = np.zeros((16, 256), dtype=np.int8)
         expect[n, k] = v
         np.testing.assert_array_equal(w, expect)
 
 
 def test_tiled_words_decode_the_page_way():
-    # random codes in {1,2,3} in every field of a 2x3-tile matrix (no padding)
+    # random codes in {1,2,3} in every field of a 2x2-tile matrix (no padding)
     g = np.random.Generator(np.random.PCG64(42))
-    N, K = 128, 192
+    N, K = 32, 512
     codes = g.integers(1, 4, size=(oracle.packed_bytes(N, K), 4)).astype(np.uint8)
     packed = (codes[:, 0] | codes[:, 1] << 2 | codes[:, 2] << 4 | codes[:, 3] << 6).astype(np.uint8)
     w = oracle.unpack_r64(packed, N, K)
     words = packed.view("<u4")
-    steps = K // 64
-    for n in (0, 1, 63, 64, 100, 127):
+    steps = K // 256
+    for n in (0, 1, 5, 15, 16, 22, 31):
         for k0 in range(0, K, 16):
-            tile = (n // 64) * steps + k0 // 64
-            slot = 4 * ((n % 64) // 4) + (k0 % 64) // 16
+            tile = (n // 16) * steps + k0 // 256
+            slot = 16 * ((n % 16) // 4) + (k0 % 256) // 16
             word_index = (tile * 1024 + 16 * slot + 4 * (n % 4)) // 4
             assert pl.decode_word(int(words[word_index])) == w[n, k0:k0 + 16].tolist()
 
 
 def test_padding_layout_and_errors():
-    N, K = 70, 80                      # two bands, two steps, ragged in both
-    assert oracle.packed_bytes(N, K) == 2 * 2 * 1024
-    assert oracle.packed_bytes(64, 64) == 1024
+    N, K = 70, 300                     # five bands, two steps, ragged in both
+    assert oracle.packed_bytes(N, K) == 5 * 2 * 1024
+    assert oracle.packed_bytes(16, 256) == 1024
     assert oracle.packed_bytes(13824, 2560) == 13824 * 2560 // 4
     p = np.zeros(oracle.packed_bytes(N, K), dtype=np.uint8)
     # fill real positions with code 2 (weight 0) byte-by-byte through the stated formula
     for n in range(N):
         for k in range(K):
-            t = (n // 64) * 2 + k // 64
+            t = (n // 16) * 2 + k // 256
             e = k % 16
-            slot = 4 * ((n % 64) // 4) + (k % 64) // 16
+            slot = 16 * ((n % 16) // 4) + (k % 256) // 16
             off = t * 1024 + 16 * slot + 4 * (n % 4) + e % 4
             p[off] |= 2 << (2 * (e // 4))
     assert (oracle.unpack_r64(p, N, K) == 0).all()
