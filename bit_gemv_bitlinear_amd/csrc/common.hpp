@@ -88,31 +88,40 @@ __device__ __forceinline__ bool bf16_rne_fast(double v, uint16_t& out) {
     return zero || (normal && !near);
 }
 
-// The same value as epilogue_bf16 without a division on the common path:
-// inv_s = fl64(1/s) is computed once per kernel, and p * inv_s lies within
-// 2^-51 (relative) of the fp64 quotient, i.e. within 4 units of its last
-// bit.  Its bf16 rounding is therefore the quotient's unless it sits within
-// 64 units of a rounding boundary (or outside bf16's normal range), in which
-// case the quotient itself is computed and rounded.
-__device__ __forceinline__ uint16_t epilogue_bf16_fast(int32_t acc, float ws, float s,
-                                                       double inv_s) {
-    const double p = static_cast<double>(acc) * static_cast<double>(ws);   // exact
+// The same value as epilogue_bf16 without a division on the common path.
+// cs = fl64(ws * fl64(1/s)) is formed once per kernel; acc * cs, rounded to
+// fp64, carries four roundings and lies within 2^-50 (relative) of the fp64
+// quotient, i.e. within 8 units of its last bit.  Its bf16 rounding is
+// therefore the quotient's unless it sits within 64 units of a rounding
+// boundary (or outside bf16's normal range), in which case the quotient
+// itself is computed and rounded.
+__device__ __forceinline__ uint16_t epilogue_bf16_scaled(int32_t acc, double cs, float ws,
+                                                         float s) {
     uint16_t out;
-    if (!bf16_rne_fast(p * inv_s, out)) out = bf16_from_double_rne(p / static_cast<double>(s));
+    if (!bf16_rne_fast(static_cast<double>(acc) * cs, out))
+        out = epilogue_bf16(acc, ws, s);
     return out;
 }
 
-// Per-activation quantisation of [W2A8] §六 item 3: round half to even of
-// x * s in fp32 (v_rndne_f32), clamped to [-128, 127].
-__device__ __forceinline__ int quant_one(float x, float s) {
-    float r = __builtin_rintf(x * s);
-    r = fminf(fmaxf(r, -128.0f), 127.0f);
-    return static_cast<int>(r);
+// Per-activation quantisation of [W2A8] §六 item 3: q = clamp(round half
+// to even of fl32(x * s), -128, 127), for finite x and s = 127 / amax with
+// |x| <= amax.  Then |fl32(x * s)| <= 127 * (1 + 2^-24)^2 < 127.5, so the
+// clamp never binds, and adding 1.5 * 2^23 rounds the product to an integer
+// (ties to even, the default rounding) in the low mantissa bits: the low
+// byte of the sum's encoding is q in two's complement.  The multiply and
+// the add must stay two roundings: fused into one FMA, a product such as
+// -63.4999997 (fp32: -63.5, so q = -64) would give -63.
+__device__ __forceinline__ uint32_t quant_byte(float x, float s) {
+#pragma clang fp contract(off)
+    const float p = x * s;
+    return __float_as_uint(p + 12582912.0f);
 }
 
-__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
-    return (static_cast<uint32_t>(a) & 0xFFu) | ((static_cast<uint32_t>(b) & 0xFFu) << 8) |
-           ((static_cast<uint32_t>(c) & 0xFFu) << 16) | ((static_cast<uint32_t>(d) & 0xFFu) << 24);
+// Four quantised values packed into an int8x4 word, value a in byte 0.
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float s) {
+    const uint32_t ab = __builtin_amdgcn_perm(quant_byte(b, s), quant_byte(a, s), 0x0C0C0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(quant_byte(d, s), quant_byte(c, s), 0x0C0C0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
 // Signed int8x4 dot product with int32 accumulate, no saturation (v_dot4_i32_i8).
@@ -120,17 +129,41 @@ __device__ __forceinline__ int dot4(int a, int b, int c) {
     return __builtin_amdgcn_sdot4(a, b, c, false);
 }
 
-// Wave-wide reductions over the 64 lanes.
+// Wave-wide reductions over the 64 lanes, for uniform control flow (every
+// lane active).  Inside each row of 16 lanes the values are combined with DPP
+// moves (swap within pairs, then within quads, then rotations by 4 and 8
+// lanes), which leaves the row's total in each of its lanes; the four row
+// totals are then read into scalar registers and combined there.  The result
+// is the same in every lane.
+template <int CTRL>
+__device__ __forceinline__ int dpp_row(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm(1, 0, 3, 2)
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm(2, 3, 0, 1)
+constexpr int kDppRowRor4 = 0x124;   // lane i <- lane (i + 4) % 16 inside each 16 lanes
+constexpr int kDppRowRor8 = 0x128;   // lane i <- lane (i + 8) % 16
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    v = fmaxf(v, __int_as_float(dpp_row<kDppQuadXor1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_row<kDppQuadXor2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_row<kDppRowRor4>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_row<kDppRowRor8>(__float_as_int(v))));
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp_row<kDppQuadXor1>(v);
+    v += dpp_row<kDppQuadXor2>(v);
+    v += dpp_row<kDppRowRor4>(v);
+    v += dpp_row<kDppRowRor8>(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
 }  // namespace bl

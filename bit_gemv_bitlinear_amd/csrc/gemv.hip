@@ -18,7 +18,10 @@
 //     lane needs one 16-byte run of activations per step;
 //   * every weight load of the wavefront is issued up front (P is a template
 //     argument, so the loads are unconditional and the compiler counts them
-//     exactly), after the activation row and the lane's weight scale;
+//     exactly), right after the lane's weight scale and its share of the
+//     activation row, and nothing is scheduled above them; the weight scale's
+//     row-to-segment division is a multiply and shift with host-made
+//     constants, so no division delays the loads;
 //   * the activation row is staged once per workgroup in LDS (zero-padded to
 //     Wb*P steps; steps past the band's end re-read its last tile and meet
 //     zero activations), read back as one 16-byte LDS load per step;
@@ -29,9 +32,14 @@
 //     term removing the +2 offset (padding code 0 contributes nothing);
 //   * the 16 lanes sharing four rows add their partial sums with DPP row
 //     operations; the Wb wavefronts of a band are added through LDS;
-//   * the epilogue multiplies by a precomputed fp64 1/s and rounds once to
+//   * the fused bf16 path quantises in the workgroup: absmax by DPP within
+//     each wavefront and LDS across them, then round-to-int by the 1.5 * 2^23
+//     addition (two roundings, as the definition has them);
+//   * the epilogue multiplies by a precomputed fp64 ws/s and rounds once to
 //     bf16, dividing only when the product lies next to a rounding boundary
-//     (so the result is that of the exact fp64 division).
+//     (so the result is that of the exact fp64 division); wavefront 0 forms
+//     ws/s and the code offset before its main loop, so the tail after the
+//     last barrier is one multiply, the rounding and the store.
 #include <algorithm>
 #include <array>
 #include <utility>
@@ -77,16 +85,6 @@ __device__ __forceinline__ void load_steps(const v4u* __restrict__ tiles, int s0
     }
 }
 
-// DPP exchanges inside a row of 16 lanes.
-template <int CTRL>
-__device__ __forceinline__ int dpp_move(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-constexpr int kQuadXor1 = 0xB1;   // quad_perm(1, 0, 3, 2)
-constexpr int kQuadXor2 = 0x4E;   // quad_perm(2, 3, 0, 1)
-constexpr int kRowRor4 = 0x124;   // lane i <- lane (i + 4) % 16 inside each 16 lanes
-constexpr int kRowRor8 = 0x128;   // lane i <- lane (i + 8) % 16
-
 // Each lane holds partial sums of the four rows of its 16-lane group (over
 // its own K chunk).  Afterwards lane l holds the full sum, over the 16 lanes,
 // of row l % 4 of the group: a reduce-scatter inside each quad, then a sum
@@ -97,14 +95,14 @@ __device__ __forceinline__ int row_group_reduce(const int (&v)[4], int lane) {
     const int send1 = b ? v[1] : v[3];
     int keep0 = b ? v[2] : v[0];
     int keep1 = b ? v[3] : v[1];
-    keep0 += dpp_move<kQuadXor2>(send0);
-    keep1 += dpp_move<kQuadXor2>(send1);
+    keep0 += dpp_row<kDppQuadXor2>(send0);
+    keep1 += dpp_row<kDppQuadXor2>(send1);
     const bool a = lane & 1;
     const int send = a ? keep0 : keep1;
     int keep = a ? keep1 : keep0;
-    keep += dpp_move<kQuadXor1>(send);     // row 2b + a = lane % 4, summed over the quad
-    keep += dpp_move<kRowRor4>(keep);
-    keep += dpp_move<kRowRor8>(keep);       // summed over the four quads
+    keep += dpp_row<kDppQuadXor1>(send);     // row 2b + a = lane % 4, summed over the quad
+    keep += dpp_row<kDppRowRor4>(keep);
+    keep += dpp_row<kDppRowRor8>(keep);       // summed over the four quads
     return keep;
 }
 
@@ -120,14 +118,10 @@ __device__ __forceinline__ float absmax8_bf16(const uint4& v, float m) {
 __device__ __forceinline__ uint2 quant8_bf16(const uint4& v, float sm) {
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
     uint2 o;
-    o.x = pack4_i8(quant_one(__uint_as_float(d[0] << 16), sm),
-                   quant_one(__uint_as_float(d[0] & 0xFFFF0000u), sm),
-                   quant_one(__uint_as_float(d[1] << 16), sm),
-                   quant_one(__uint_as_float(d[1] & 0xFFFF0000u), sm));
-    o.y = pack4_i8(quant_one(__uint_as_float(d[2] << 16), sm),
-                   quant_one(__uint_as_float(d[2] & 0xFFFF0000u), sm),
-                   quant_one(__uint_as_float(d[3] << 16), sm),
-                   quant_one(__uint_as_float(d[3] & 0xFFFF0000u), sm));
+    o.x = quant4(__uint_as_float(d[0] << 16), __uint_as_float(d[0] & 0xFFFF0000u),
+                 __uint_as_float(d[1] << 16), __uint_as_float(d[1] & 0xFFFF0000u), sm);
+    o.y = quant4(__uint_as_float(d[2] << 16), __uint_as_float(d[2] & 0xFFFF0000u),
+                 __uint_as_float(d[3] << 16), __uint_as_float(d[3] & 0xFFFF0000u), sm);
     return o;
 }
 
@@ -135,7 +129,8 @@ __device__ __forceinline__ int sum_i8x4(uint32_t d, int acc) {
     return dot4(static_cast<int>(d), 0x01010101, acc);
 }
 
-// seg = N / ws_num: rows per weight scale.  B bands per workgroup, 2^lw
+// Row n's weight scale is ws[n / seg], seg = N / ws_num, found as
+// (n * seg_mul) >> seg_shift (see seg_divisor()).  B bands per workgroup, 2^lw
 // wavefronts per band (blockDim.x = 64 * B * 2^lw), P K-steps per wavefront.
 // FUSED = false: xin is int8 activations with scale s_in[0].
 // FUSED = true:  xin is bf16; the workgroup quantises it (per-token absmax,
@@ -143,7 +138,7 @@ __device__ __forceinline__ int sum_i8x4(uint32_t d, int acc) {
 template <int P, bool FUSED>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     const void* __restrict__ xin, const v4u* __restrict__ packed, const float* __restrict__ s_in,
-    const uint16_t* __restrict__ ws, int seg, uint16_t* __restrict__ y,
+    const uint16_t* __restrict__ ws, uint32_t seg_mul, int seg_shift, uint16_t* __restrict__ y,
     int32_t* __restrict__ acc, int8_t* __restrict__ q_out, float* __restrict__ s_out, int N,
     int K, int B, int lw) {
     extern __shared__ int4 act[];   // Wb*P*16 16-byte chunks: the int8 row, zero-padded
@@ -167,7 +162,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     //    first (so that waiting for them does not wait for the weights), then
     //    every weight load of this wavefront.
     const int n_out = static_cast<int>(blockIdx.x) * B * kTileRows + tid;   // tid < 16*B writes
-    const uint16_t wsb = ws[min(n_out, N - 1) / seg];   // unconditional: no branch, no early wait
+    const uint32_t n_ws = static_cast<uint32_t>(min(n_out, N - 1));
+    // unconditional: no branch, no early wait
+    const uint16_t wsb = ws[(static_cast<uint64_t>(n_ws) * seg_mul) >> seg_shift];
     uint4 xv[kCached];
     const int n_in = FUSED ? (K >> 3) : n16;   // 16-byte input chunks
     const uint4* x16 = reinterpret_cast<const uint4*>(xin);
@@ -180,6 +177,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     const v4u* tiles = packed + static_cast<size_t>(band) * S * 64 + lane;
     v4u w[P];
     load_steps<P>(tiles, s0, S - 1, w);
+    // Nothing may be scheduled above this point: otherwise the compiler may
+    // start on the activations first, and the wait for them would hold back
+    // the remaining weight loads by a full memory latency.
+    __builtin_amdgcn_sched_barrier(0);
 
     // 2. Stage the int8 row in LDS and sum it (for the +2 code offset).
     int xs = 0;
@@ -202,7 +203,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     } else {
         float amax = 0.0f;
 #pragma unroll
-        for (int c = 0; c < kCached; ++c) amax = absmax8_bf16(xv[c], amax);
+        for (int c = 0; c < kCached; ++c)
+            if (tid + c * nthreads < n_in) amax = absmax8_bf16(xv[c], amax);
         for (int idx = tid + kCached * nthreads; idx < n_in; idx += nthreads)
             amax = absmax8_bf16(x16[idx], amax);
         amax = wave_max(amax);
@@ -232,18 +234,21 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
         if (blockIdx.x == 0 && s_out != nullptr && tid == 0) s_out[0] = sm;
     }
     for (int i = n16 + tid; i < padded16; i += nthreads) act[i] = make_int4(0, 0, 0, 0);
-    // 1/s for the epilogue, computed here while the weights are in flight;
-    // the empty asm statement keeps the compiler from sinking the division
-    // past the barriers to its use.
-    double inv_s = 1.0 / static_cast<double>(sm);
-    asm volatile("" : "+v"(inv_s));
     xs = wave_sum(xs);
     if (lane == 0) xsum_sh[wave] = xs;
     __syncthreads();
-    // The code offset correction, -2 * sum(x), summed here while the weights
-    // are still in flight rather than after the last barrier.
+    // Wavefront 0 alone needs the epilogue's factors: the scale ws / s (as
+    // fl64(ws * fl64(1/s))) and the code offset correction -2 * sum(x).  It
+    // forms them here, while the weights are still in flight, rather than
+    // after the last barrier; the empty asm statement keeps the compiler from
+    // sinking them past the barrier to their use.
+    double cs = 0.0;
     int offset = 0;
-    for (int i = 0; i < W; ++i) offset -= 2 * xsum_sh[i];
+    if (wave == 0) {
+        cs = static_cast<double>(bf16_to_float(wsb)) * (1.0 / static_cast<double>(sm));
+        for (int i = 0; i < W; ++i) offset -= 2 * xsum_sh[i];
+        asm volatile("" : "+v"(cs), "+v"(offset));
+    }
 
     // 3. P steps of 4 rows x 16 K per lane.
     RowAcc r;
@@ -269,18 +274,31 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
         int total = offset;
         for (int j = 0; j < Wb; ++j) total += part_sh[first + j][slot];
         if (bw < B && n_out < N) {
-            y[n_out] = epilogue_bf16_fast(total, bf16_to_float(wsb), sm, inv_s);
+            y[n_out] = epilogue_bf16_scaled(total, cs, bf16_to_float(wsb), sm);
             if (acc) acc[n_out] = total;
         }
     }
+}
+
+// n / d == (n * mul) >> shift for every 0 <= n < 2^24 (N <= 2^24): with
+// l = ceil(log2 d), shift = 24 + l and mul = ceil(2^shift / d), the excess
+// mul * d - 2^shift is at most d - 1 <= 2^l = 2^(shift - 24), the condition
+// under which the product gives exact quotients of 24-bit numerators
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).  mul < 2^25, so n * mul < 2^49.
+void seg_divisor(int d, uint32_t& mul, int& shift) {
+    int l = 0;
+    while ((1 << l) < d) ++l;
+    shift = 24 + l;
+    mul = static_cast<uint32_t>(((1ull << shift) + static_cast<uint64_t>(d) - 1) / d);
 }
 
 constexpr int kMaxSteps = 20;
 constexpr int kMinGroups = 200;     // workgroups wanted in flight (256 CUs)
 constexpr int kTargetSteps = 9;     // K steps per wavefront aimed at
 
-using GemvFn = void (*)(const void*, const v4u*, const float*, const uint16_t*, int, uint16_t*,
-                        int32_t*, int8_t*, float*, int, int, int, int);
+using GemvFn = void (*)(const void*, const v4u*, const float*, const uint16_t*, uint32_t, int,
+                        uint16_t*, int32_t*, int8_t*, float*, int, int, int, int);
 
 template <bool FUSED, int... Ps>
 constexpr std::array<GemvFn, sizeof...(Ps)> kernel_table(std::integer_sequence<int, Ps...>) {
@@ -304,8 +322,12 @@ hipError_t launch(bool fused, const void* x, const uint8_t* packed, const float*
     while ((1 << lw) < wb) ++lw;
     const size_t lds = static_cast<size_t>(wb) * g.steps * kTileK;
     const GemvFn fn = fused ? kBf16Kernels[g.steps - 1] : kI8Kernels[g.steps - 1];
+    uint32_t seg_mul;
+    int seg_shift;
+    seg_divisor(N / ws_num, seg_mul, seg_shift);
     fn<<<groups, g.waves * 64, lds, stream>>>(x, reinterpret_cast<const v4u*>(packed), s, ws,
-                                             N / ws_num, y, acc, q_out, s_out, N, K, g.bands, lw);
+                                             seg_mul, seg_shift, y, acc, q_out, s_out, N, K,
+                                             g.bands, lw);
     return hipGetLastError();
 }
 

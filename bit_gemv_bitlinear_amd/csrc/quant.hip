@@ -65,10 +65,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const void* __rest
         float v[8];
         load8<BF16>(x, row8 + c, v);
         uint2 o;
-        o.x = pack4_i8(quant_one(v[0], sm), quant_one(v[1], sm), quant_one(v[2], sm),
-                       quant_one(v[3], sm));
-        o.y = pack4_i8(quant_one(v[4], sm), quant_one(v[5], sm), quant_one(v[6], sm),
-                       quant_one(v[7], sm));
+        o.x = quant4(v[0], v[1], v[2], v[3], sm);
+        o.y = quant4(v[4], v[5], v[6], v[7], sm);
         qrow[c] = o;
     }
     if (threadIdx.x == 0) s[m] = sm;

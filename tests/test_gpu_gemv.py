@@ -148,6 +148,29 @@ def test_fused_bf16(bl, name, N, K, ws_num):
     assert assert_bf16_close(host_bits(y), y_o, max_ulp=1) == 0
 
 
+@pytest.mark.parametrize("N,K", [(640, 2560), (13824, 2560), (2560, 6912)])
+def test_fused_product_ties(bl, N, K):
+    # activations whose products x * s sit on fp32 .5 ties (see quant_cases):
+    # the in-kernel quantiser must round twice, as the definition does
+    import torch
+    from quant_cases import tie_rows
+    print(f"fused product ties N={N} K={K}", flush=True)
+    xb = tie_rows(1, K, seed=N + K)
+    c = synth.make_int8_gemv("ties", 1, N, K, 1, synth.seed_for(8, 0, N % 101))
+    packed = bl.pack_ternary_weights(dev(c.w))
+    q = torch.empty((1, K), dtype=torch.int8, device="cuda")
+    s = torch.empty((1,), dtype=torch.float32, device="cuda")
+    acc = torch.empty((1, N), dtype=torch.int32, device="cuda")
+    y = bl.bitlinear_bf16_i8xi2(bf16_dev(xb), packed, bf16_dev(c.ws), N, 1, q_out=q, s_out=s,
+                                acc=acc)
+    torch.cuda.synchronize()
+    qo, so, acc_o, y_o = oracle.bitlinear_bf16(xb, c.w, c.ws, 1)
+    np.testing.assert_array_equal(q.cpu().numpy(), qo)
+    np.testing.assert_array_equal(s.cpu().numpy(), so)
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_o)
+    assert assert_bf16_close(host_bits(y), y_o, max_ulp=1) == 0
+
+
 def test_fused_without_optional_outputs(bl):
     import torch
     print("fused_bf16 no optional outputs", flush=True)

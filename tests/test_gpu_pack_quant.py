@@ -113,3 +113,17 @@ def test_quant_many_random_scales_bit_exact(bl):
     qo, so = oracle.quant_absmax_i8(x)
     np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
     np.testing.assert_array_equal(q.cpu().numpy(), qo)
+
+
+def test_quant_bf16_product_ties(bl):
+    # x * s lands on an fp32 .5 tie that the exact product misses: the two
+    # roundings of the definition must not be fused into one
+    import torch
+    from quant_cases import tie_rows
+    print("quant bf16 product ties", flush=True)
+    xb = tie_rows(16, 2560, seed=5)
+    q, s = bl.quantize_act_absmax_i8(bf16_dev(xb))
+    torch.cuda.synchronize()
+    qo, so = oracle.quant_absmax_i8(xb, bf16=True)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    np.testing.assert_array_equal(q.cpu().numpy(), qo)
