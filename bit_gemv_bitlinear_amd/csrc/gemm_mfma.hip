@@ -9,8 +9,8 @@
 //
 // Mapping (this library's design):
 //   * workgroup (column, mchunk): four 16-row bands = 64 output rows n x up
-//     to 64 rows m, 4 wavefronts that split the K steps (64 K each) between
-//     them;
+//     to 64 rows m (MT tiles of 16), 4 or 8 wavefronts that split the 64-K
+//     steps between them, PS consecutive steps per wavefront and chunk;
 //   * per K step a wavefront reads, for each of the four bands t, one word per
 //     lane: lane (j = lane%16, g = lane/16) takes the word of row j for the
 //     16-wide K chunk g of this step -- byte 256*(j/4) + 64*(step%4) + 16*g +
@@ -18,10 +18,20 @@
 //     v_mfma_i32_16x16x64_i8 for that band (16 K of one column);
 //     v_perm_b32 turns the 2-bit codes into signed int8 weights (code 0, the
 //     padding, becomes 0) after each shift-and-mask of [W2A8] §5.2;
-//   * the A operand (16 rows m x 64 K) is read straight from the int8
-//     activations, 16 bytes per lane, zero outside M and K;
-//   * the four wavefronts' int32 tiles are added with LDS atomics (exact in
-//     any order), then the fp64 epilogue writes bf16 (and optionally int32).
+//   * all PS x 4 weight words of a chunk are loaded up front (PS is a
+//     template argument, so the loads are unconditional: steps past the end
+//     re-read the last step and add zero), and so are the
+//     chunk's PS x MT A operands (16 rows m x 64 K, 16 bytes per lane
+//     straight from the int8 activations, zero outside M and K): both come
+//     from far enough away that only loads issued together hide their
+//     latency (PS * MT <= 20 bounds the registers);
+//   * the wavefronts' int32 tiles are added with LDS atomics (exact in any
+//     order), then the epilogue writes bf16 through the division-free fp64
+//     rounding (and optionally int32).
+#include <algorithm>
+#include <array>
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,8 +39,9 @@ namespace bl {
 
 namespace {
 
-constexpr int kMfmaWaves = 4;
-constexpr int kMfmaThreads = kMfmaWaves * 64;
+constexpr int kMfmaMaxWaves = 8;
+constexpr int kMfmaMaxSteps = 16;   // 64-K steps per wavefront and chunk
+constexpr int kMfmaMaxAFrags = 20;  // PS * MT: A operands held per wavefront
 
 __device__ __forceinline__ v4i decode_b(uint32_t w) {
     v4i b;
@@ -41,26 +52,56 @@ __device__ __forceinline__ v4i decode_b(uint32_t w) {
     return b;
 }
 
-// MT = number of 16-row m tiles this workgroup covers (1..4).
+// A operands of one 64-K step for MT m tiles: 16 bytes of row m at K offset
+// 64*st + 16*g, from clamped addresses so that the loads are unconditional.
+// Nothing needs zeroing: a row m >= M (read as row M - 1) only reaches its
+// own outputs, which are not written; K positions >= K in the last step
+// meet padding codes, which decode to 0; whole steps past the end are
+// zeroed where they are used.
 template <int MT>
-__global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
-    const int8_t* __restrict__ xq, const uint8_t* __restrict__ packed, const float* __restrict__ s,
-    const uint16_t* __restrict__ ws, int ws_num, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc_out, int M, int N, int K) {
+__device__ __forceinline__ void load_a(const int8_t* const (&row)[MT], int st, int g, int K,
+                                       v4i (&a)[MT]) {
+    const int kc = min(st * 64 + 16 * g, K - 16);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a[mt] = *reinterpret_cast<const v4i*>(row[mt] + kc);
+}
+
+// MT = number of 16-row m tiles this workgroup covers (1..4); PS = 64-K steps
+// per wavefront and chunk.  blockDim.x = 64 * (4 or 8).
+template <int MT, int PS>
+__global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
+    const int8_t* __restrict__ xq, const uint32_t* __restrict__ words,
+    const float* __restrict__ s, const uint16_t* __restrict__ ws, uint32_t seg_mul,
+    int seg_shift, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, int M, int N, int K) {
     __shared__ int red[MT * 16][64];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ double inv_s_sh[MT * 16];
+    const int nthreads = blockDim.x;
+    const int nwaves = nthreads >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = blockIdx.x;                      // 64 output rows = 4 bands
     const int nbands = (N + kTileRows - 1) / kTileRows;
     const int m0 = blockIdx.y * 64;
     const int S256 = (K + kTileK - 1) / kTileK;      // 1 KiB tiles per band
-    const int S = (K + 63) / 64;                     // 64-K MFMA steps
-    const int s0 = (S * wave) / kMfmaWaves;
-    const int s1 = (S * (wave + 1)) / kMfmaWaves;
+    const int S64 = (K + 63) / 64;                   // 64-K MFMA steps
     const int j = lane & 15;
     const int g = lane >> 4;
 
-    for (int i = threadIdx.x; i < MT * 16 * 64; i += kMfmaThreads) (&red[0][0])[i] = 0;
+    for (int i = tid; i < MT * 16 * 16; i += nthreads) reinterpret_cast<int4*>(&red[0][0])[i] = int4{0, 0, 0, 0};
+    // the activation scale of m row tid (if any) is loaded now and inverted
+    // after the main loop, so that neither waits in front of the weight loads
+    const float s_row = s[min(m0 + min(tid, MT * 16 - 1), M - 1)];
+
+    const int8_t* row[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        row[mt] = xq + static_cast<size_t>(min(m0 + 16 * mt + j, M - 1)) * K;
+    size_t band_base[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        band_base[t] = static_cast<size_t>(min(4 * col + t, nbands - 1)) * S256 * (kTileBytes / 4);
+    const int lane_word = 64 * (j >> 2) + 4 * g + (j & 3);
 
     v4i c[MT][4];
 #pragma unroll
@@ -68,35 +109,41 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t) c[mt][t] = v4i{0, 0, 0, 0};
 
-    const uint32_t* words = reinterpret_cast<const uint32_t*>(packed);
-    size_t band_base[4];
+    for (int base = wave * PS; base < S64; base += nwaves * PS) {
+        uint32_t bw[PS][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-        band_base[t] = static_cast<size_t>(min(4 * col + t, nbands - 1)) * S256 * (kTileBytes / 4);
-    const int lane_word = 64 * (j >> 2) + 4 * g + (j & 3);
-    for (int st = s0; st < s1; ++st) {
-        const size_t step_word = static_cast<size_t>(st >> 2) * (kTileBytes / 4) + 16 * (st & 3) + lane_word;
-        uint32_t bw[4];
+        for (int p = 0; p < PS; ++p) {
+            const int st = min(base + p, S64 - 1);
+            const size_t step_word =
+                static_cast<size_t>(st >> 2) * (kTileBytes / 4) + 16 * (st & 3) + lane_word;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bw[t] = __builtin_nontemporal_load(words + band_base[t] + step_word);
-        v4i a[MT];
-        const int k = st * 64 + 16 * g;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = m0 + 16 * mt + j;
-            a[mt] = v4i{0, 0, 0, 0};
-            if (m < M && k < K)
-                a[mt] = *reinterpret_cast<const v4i*>(xq + static_cast<size_t>(m) * K + k);
+            for (int t = 0; t < 4; ++t)
+                bw[p][t] = __builtin_nontemporal_load(words + band_base[t] + step_word);
         }
+        v4i a[PS][MT];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const v4i b = decode_b(bw[t]);
+        for (int p = 0; p < PS; ++p) load_a<MT>(row, base + p, g, K, a[p]);
+        // Nothing may be scheduled above this point: the first wait for an
+        // operand would otherwise hold back the remaining loads.
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                c[mt][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mt], b, c[mt][t], 0, 0, 0);
+        for (int p = 0; p < PS; ++p) {
+            // a step past the end (a re-read of the last one) must add nothing
+            const bool live = base + p < S64;
+            v4i ap[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) ap[mt] = live ? a[p][mt] : v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const v4i b = decode_b(bw[p][t]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    c[mt][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[mt], b, c[mt][t], 0, 0, 0);
+            }
         }
     }
-    __syncthreads();   // red[] zeroed by every thread before any atomics
+    if (tid < MT * 16) inv_s_sh[tid] = 1.0 / static_cast<double>(s_row);
+    __syncthreads();   // red[] zeroed and inv_s_sh[] written before use
     // D layout of a 16x16 tile: lane (j, g), register v -> row 4g + v, column j.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -108,45 +155,65 @@ __global__ __launch_bounds__(kMfmaThreads) void gemm_mfma_kernel(
             atomicAdd(&red[16 * mt + 4 * g + 3][16 * t + j], c[mt][t].w);
         }
     __syncthreads();
-    const int seg = N / ws_num;
-    for (int i = threadIdx.x; i < MT * 16 * 64; i += kMfmaThreads) {
+    // Every thread keeps one output column (the stride is a multiple of 64).
+    const int nl = tid & 63;
+    const int n = col * 64 + nl;
+    const float wsf = bf16_to_float(ws[(static_cast<uint64_t>(min(n, N - 1)) * seg_mul) >> seg_shift]);
+    for (int i = tid; i < MT * 16 * 64; i += nthreads) {
         const int ml = i >> 6;
-        const int nl = i & 63;
         const int m = m0 + ml;
-        const int n = col * 64 + nl;
         if (m < M && n < N) {
             const int32_t total = red[ml][nl];
             const size_t o = static_cast<size_t>(m) * N + n;
-            y[o] = epilogue_bf16(total, bf16_to_float(ws[n / seg]), s[m]);
+            const double cs = static_cast<double>(wsf) * inv_s_sh[ml];
+            y[o] = epilogue_bf16_scaled(total, cs, wsf, s[m]);
             if (acc_out) acc_out[o] = total;
         }
     }
 }
 
-template <int MT>
-hipError_t launch_mt(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,
-                     int ws_num, uint16_t* y, int32_t* acc, int M, int N, int K,
-                     hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((M + 63) / 64));
-    gemm_mfma_kernel<MT><<<grid, kMfmaThreads, 0, stream>>>(xq, packed, s, ws, ws_num, y, acc, M,
-                                                             N, K);
-    return hipGetLastError();
+using MfmaFn = void (*)(const int8_t*, const uint32_t*, const float*, const uint16_t*, uint32_t,
+                        int, uint16_t*, int32_t*, int, int, int);
+
+// Entries past the A-operand budget (PS * MT > kMfmaMaxAFrags) are never
+// selected; they repeat the largest allowed PS so that no such kernel exists.
+template <int MT, int... Ps>
+constexpr std::array<MfmaFn, sizeof...(Ps)> mfma_table(std::integer_sequence<int, Ps...>) {
+    return {{&gemm_mfma_kernel<MT, std::min(Ps + 1, kMfmaMaxAFrags / MT)>...}};
 }
+
+const std::array<std::array<MfmaFn, kMfmaMaxSteps>, 4> kMfmaKernels = {{
+    mfma_table<1>(std::make_integer_sequence<int, kMfmaMaxSteps>{}),
+    mfma_table<2>(std::make_integer_sequence<int, kMfmaMaxSteps>{}),
+    mfma_table<3>(std::make_integer_sequence<int, kMfmaMaxSteps>{}),
+    mfma_table<4>(std::make_integer_sequence<int, kMfmaMaxSteps>{}),
+}};
+
+constexpr int kMfmaMinGroups = 128;   // fewer workgroups than this: 8 wavefronts each
 
 }  // namespace
 
 hipError_t launch_gemm_mfma(const int8_t* xq, const uint8_t* packed, const float* s,
                             const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int M,
                             int N, int K, hipStream_t stream) {
-    // m tiles needed by the widest workgroup column (all columns but the last
-    // are full 64-row chunks).
+    // m tiles needed by the widest workgroup (all but the last are full 64-row chunks)
     const int mt = (M >= 64) ? 4 : (M + 15) / 16;
-    switch (mt) {
-        case 1: return launch_mt<1>(xq, packed, s, ws, ws_num, y, acc, M, N, K, stream);
-        case 2: return launch_mt<2>(xq, packed, s, ws, ws_num, y, acc, M, N, K, stream);
-        case 3: return launch_mt<3>(xq, packed, s, ws, ws_num, y, acc, M, N, K, stream);
-        default: return launch_mt<4>(xq, packed, s, ws, ws_num, y, acc, M, N, K, stream);
-    }
+    const dim3 grid(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((M + 63) / 64));
+    const int S64 = (K + 63) / 64;
+    const int max_ps = std::min(kMfmaMaxSteps, kMfmaMaxAFrags / mt);
+    // 8 wavefronts when the grid is small or 4 would need a second chunk
+    const int waves =
+        (grid.x * grid.y < kMfmaMinGroups || (S64 + 3) / 4 > max_ps) ? 8 : 4;
+    const int per_wave = (S64 + waves - 1) / waves;
+    const int chunks = (per_wave + max_ps - 1) / max_ps;
+    const int ps = (S64 + waves * chunks - 1) / (waves * chunks);
+    uint32_t seg_mul;
+    int seg_shift;
+    seg_divisor(N / ws_num, seg_mul, seg_shift);
+    const MfmaFn fn = kMfmaKernels[mt - 1][ps - 1];
+    fn<<<grid, waves * 64, 0, stream>>>(xq, reinterpret_cast<const uint32_t*>(packed), s, ws,
+                                        seg_mul, seg_shift, y, acc, M, N, K);
+    return hipGetLastError();
 }
 
 }  // namespace bl

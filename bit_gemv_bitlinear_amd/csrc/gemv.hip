@@ -280,19 +280,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     }
 }
 
-// n / d == (n * mul) >> shift for every 0 <= n < 2^24 (N <= 2^24): with
-// l = ceil(log2 d), shift = 24 + l and mul = ceil(2^shift / d), the excess
-// mul * d - 2^shift is at most d - 1 <= 2^l = 2^(shift - 24), the condition
-// under which the product gives exact quotients of 24-bit numerators
-// (Granlund and Montgomery, "Division by invariant integers using
-// multiplication", 1994).  mul < 2^25, so n * mul < 2^49.
-void seg_divisor(int d, uint32_t& mul, int& shift) {
-    int l = 0;
-    while ((1 << l) < d) ++l;
-    shift = 24 + l;
-    mul = static_cast<uint32_t>(((1ull << shift) + static_cast<uint64_t>(d) - 1) / d);
-}
-
 constexpr int kMaxSteps = 20;
 constexpr int kMinGroups = 200;     // workgroups wanted in flight (256 CUs)
 constexpr int kTargetSteps = 9;     // K steps per wavefront aimed at
@@ -332,6 +319,19 @@ hipError_t launch(bool fused, const void* x, const uint8_t* packed, const float*
 }
 
 }  // namespace
+
+// n / d == (n * mul) >> shift for every 0 <= n < 2^24 (N <= 2^24): with
+// l = ceil(log2 d), shift = 24 + l and mul = ceil(2^shift / d), the excess
+// mul * d - 2^shift is at most d - 1 <= 2^l = 2^(shift - 24), the condition
+// under which the product gives exact quotients of 24-bit numerators
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).  mul < 2^25, so n * mul < 2^49.
+void seg_divisor(int d, uint32_t& mul, int& shift) {
+    int l = 0;
+    while ((1 << l) < d) ++l;
+    shift = 24 + l;
+    mul = static_cast<uint32_t>(((1ull << shift) + static_cast<uint64_t>(d) - 1) / d);
+}
 
 GemvShape gemv_shape(int N, int K) {
     const int S = (K + kTileK - 1) / kTileK;

@@ -18,6 +18,10 @@ int64_t pack_host(const int8_t* w, uint8_t* packed, int N, int K);
 hipError_t launch_quant(const void* x, int x_is_bf16, int8_t* q, float* s, int M, int K,
                         hipStream_t stream);
 
+// Row n's weight-scale index n / d (d = N / ws_num) as (n * mul) >> shift,
+// exact for every 0 <= n < 2^24.
+void seg_divisor(int d, uint32_t& mul, int& shift);
+
 // M == 1 GEMV geometry: `waves` wavefronts per workgroup covering `bands`
 // 16-row bands, `steps` K steps (256 K each) per wavefront; waves == 0 when
 // K is beyond the GEMV kernels (K > kGemvMaxK), which then leave M == 1 to

@@ -1,10 +1,12 @@
-"""Structure of the compiled GEMV kernels (host-only: hipcc cross-compiles gfx950).
+"""Structure of the compiled kernels (host-only: hipcc cross-compiles gfx950).
 
 Every gemv_kernel<P, FUSED> must issue all P of a wavefront's weight loads
-(the non-temporal 16-byte loads) before its first wait on vector memory:
-the waits count loads in issue order, so a weight load issued after the
-first wait is held back by a full memory latency.  The compiler is free to
-schedule otherwise, so this is checked on the assembly it produces.
+(the non-temporal 16-byte loads) before its first wait on vector memory, and
+every gemm_mfma_kernel<MT, PS> all 4 * PS of its weight words (non-temporal
+4-byte loads) and all PS * MT of its activation operands: the waits count
+loads in issue order, so a load issued after the first wait is held back by
+a full memory latency.  The compiler is
+free to schedule otherwise, so this is checked on the assembly it produces.
 """
 import os
 import re
@@ -17,17 +19,26 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(ROOT, "bit_gemv_bitlinear_amd", "csrc")
 
 
-@pytest.fixture(scope="module")
-def gemv_asm(tmp_path_factory):
+def _asm(tmp_path_factory, source):
     from bit_gemv_bitlinear_amd import build
     if not os.path.exists(build.HIPCC):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "gemv.s"
+    out = tmp_path_factory.mktemp("isa") / source.replace(".hip", ".s")
     flags = [f for f in build.FLAGS if f != "-fPIC"]
-    cmd = [build.HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemv.hip"),
+    cmd = [build.HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, source),
            "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def gemv_asm(tmp_path_factory):
+    return _asm(tmp_path_factory, "gemv.hip")
+
+
+@pytest.fixture(scope="module")
+def mfma_asm(tmp_path_factory):
+    return _asm(tmp_path_factory, "gemm_mfma.hip")
 
 
 def test_weight_loads_issued_before_first_wait(gemv_asm):
@@ -42,3 +53,20 @@ def test_weight_loads_issued_before_first_wait(gemv_asm):
         if issued != P:
             late.append((P, m.group(3), issued))
     assert not late, f"(P, fused, weight loads before the first wait): {late}"
+
+
+def test_mfma_operand_loads_issued_before_first_wait(mfma_asm):
+    kernels = list(re.finditer(r"^(_ZN\S*gemm_mfma_kernelILi(\d+)ELi(\d+)E\S*):", mfma_asm, re.M))
+    # MT = 1..4 m tiles, PS = 1..min(16, 20 / MT) steps
+    assert sorted((int(m.group(2)), int(m.group(3))) for m in kernels) == \
+        [(mt, ps) for mt in range(1, 5) for ps in range(1, min(16, 20 // mt) + 1)]
+    late = []
+    for m in kernels:
+        MT, PS = int(m.group(2)), int(m.group(3))
+        body = mfma_asm[m.end():mfma_asm.index("s_endpgm", m.end())]
+        first_wait = body.index("s_waitcnt vmcnt")
+        weights = len(re.findall(r"global_load_dword [^\n]* nt\b", body[:first_wait]))
+        acts = len(re.findall(r"global_load_dwordx4 ", body[:first_wait]))
+        if weights != 4 * PS or acts != PS * MT:
+            late.append((MT, PS, weights, acts))
+    assert not late, f"(MT, PS, weight words, A operands before the first wait): {late}"
