@@ -42,6 +42,9 @@ namespace {
 constexpr int kMfmaMaxWaves = 8;
 constexpr int kMfmaMaxSteps = 16;   // 64-K steps per wavefront and chunk
 constexpr int kMfmaMaxAFrags = 20;  // PS * MT: A operands held per wavefront
+// Row pitch of the LDS reduction tile: 64 columns + 4, so that the four lane
+// groups adding the same column of a 16x16 tile land in different banks.
+constexpr int kRedPitch = 68;
 
 __device__ __forceinline__ v4i decode_b(uint32_t w) {
     v4i b;
@@ -73,8 +76,9 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
     const int8_t* __restrict__ xq, const uint32_t* __restrict__ words,
     const float* __restrict__ s, const uint16_t* __restrict__ ws, uint32_t seg_mul,
     int seg_shift, uint16_t* __restrict__ y, int32_t* __restrict__ acc_out, int M, int N, int K) {
-    __shared__ int red[MT * 16][64];
+    __shared__ __align__(16) int red[MT * 16][kRedPitch];
     __shared__ double inv_s_sh[MT * 16];
+    __shared__ float s_sh[MT * 16];
     const int nthreads = blockDim.x;
     const int nwaves = nthreads >> 6;
     const int tid = threadIdx.x;
@@ -88,7 +92,8 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
     const int j = lane & 15;
     const int g = lane >> 4;
 
-    for (int i = tid; i < MT * 16 * 16; i += nthreads) reinterpret_cast<int4*>(&red[0][0])[i] = int4{0, 0, 0, 0};
+    for (int i = tid; i < MT * 16 * kRedPitch / 4; i += nthreads)
+        reinterpret_cast<int4*>(&red[0][0])[i] = int4{0, 0, 0, 0};
     // the activation scale of m row tid (if any) is loaded now and inverted
     // after the main loop, so that neither waits in front of the weight loads
     const float s_row = s[min(m0 + min(tid, MT * 16 - 1), M - 1)];
@@ -110,6 +115,18 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
         for (int t = 0; t < 4; ++t) c[mt][t] = v4i{0, 0, 0, 0};
 
     for (int base = wave * PS; base < S64; base += nwaves * PS) {
+        // Waits count loads in issue order.  With the A operands first, step
+        // p waits for its own weight words only, so the MFMAs run while the
+        // weights stream in; but for MT >= 3 the A operands (each workgroup
+        // reads all of A) outweigh the weights several times over, and
+        // issued first they hold the weight stream back, so there the
+        // weights go first.
+        constexpr bool kAFirst = MT <= 2;
+        v4i a[PS][MT];
+        if constexpr (kAFirst) {
+#pragma unroll
+            for (int p = 0; p < PS; ++p) load_a<MT>(row, base + p, g, K, a[p]);
+        }
         uint32_t bw[PS][4];
 #pragma unroll
         for (int p = 0; p < PS; ++p) {
@@ -120,9 +137,10 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
             for (int t = 0; t < 4; ++t)
                 bw[p][t] = __builtin_nontemporal_load(words + band_base[t] + step_word);
         }
-        v4i a[PS][MT];
+        if constexpr (!kAFirst) {
 #pragma unroll
-        for (int p = 0; p < PS; ++p) load_a<MT>(row, base + p, g, K, a[p]);
+            for (int p = 0; p < PS; ++p) load_a<MT>(row, base + p, g, K, a[p]);
+        }
         // Nothing may be scheduled above this point: the first wait for an
         // operand would otherwise hold back the remaining loads.
         __builtin_amdgcn_sched_barrier(0);
@@ -142,7 +160,10 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
             }
         }
     }
-    if (tid < MT * 16) inv_s_sh[tid] = 1.0 / static_cast<double>(s_row);
+    if (tid < MT * 16) {
+        inv_s_sh[tid] = 1.0 / static_cast<double>(s_row);
+        s_sh[tid] = s_row;
+    }
     __syncthreads();   // red[] zeroed and inv_s_sh[] written before use
     // D layout of a 16x16 tile: lane (j, g), register v -> row 4g + v, column j.
 #pragma unroll
@@ -155,19 +176,50 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
             atomicAdd(&red[16 * mt + 4 * g + 3][16 * t + j], c[mt][t].w);
         }
     __syncthreads();
-    // Every thread keeps one output column (the stride is a multiple of 64).
-    const int nl = tid & 63;
-    const int n = col * 64 + nl;
-    const float wsf = bf16_to_float(ws[(static_cast<uint64_t>(min(n, N - 1)) * seg_mul) >> seg_shift]);
-    for (int i = tid; i < MT * 16 * 64; i += nthreads) {
-        const int ml = i >> 6;
+    // Each thread writes four consecutive outputs of one row m: columns
+    // n0 .. n0 + 3 (fixed per thread, the stride being a multiple of 16),
+    // with 8-byte (bf16) and 16-byte (int32) stores where the row is aligned
+    // for them.
+    const int c4 = (tid & 15) * 4;
+    const int n0 = col * 64 + c4;
+    float wsf[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        wsf[e] = bf16_to_float(
+            ws[(static_cast<uint64_t>(min(n0 + e, N - 1)) * seg_mul) >> seg_shift]);
+    for (int i = tid; i < MT * 16 * 16; i += nthreads) {
+        const int ml = i >> 4;
         const int m = m0 + ml;
-        if (m < M && n < N) {
-            const int32_t total = red[ml][nl];
-            const size_t o = static_cast<size_t>(m) * N + n;
-            const double cs = static_cast<double>(wsf) * inv_s_sh[ml];
-            y[o] = epilogue_bf16_scaled(total, cs, wsf, s[m]);
-            if (acc_out) acc_out[o] = total;
+        if (m < M && n0 < N) {
+            const int4 t = *reinterpret_cast<const int4*>(&red[ml][c4]);
+            const double inv = inv_s_sh[ml];
+            const float sm = s_sh[ml];
+            const uint32_t o0 = epilogue_bf16_scaled(t.x, static_cast<double>(wsf[0]) * inv, wsf[0], sm);
+            const uint32_t o1 = epilogue_bf16_scaled(t.y, static_cast<double>(wsf[1]) * inv, wsf[1], sm);
+            const uint32_t o2 = epilogue_bf16_scaled(t.z, static_cast<double>(wsf[2]) * inv, wsf[2], sm);
+            const uint32_t o3 = epilogue_bf16_scaled(t.w, static_cast<double>(wsf[3]) * inv, wsf[3], sm);
+            const size_t o = static_cast<size_t>(m) * N + n0;
+            uint16_t* yo = y + o;
+            const bool full = n0 + 4 <= N;
+            if (full && (reinterpret_cast<uintptr_t>(yo) & 7) == 0) {
+                *reinterpret_cast<uint2*>(yo) = uint2{o0 | (o1 << 16), o2 | (o3 << 16)};
+            } else {
+                yo[0] = static_cast<uint16_t>(o0);
+                if (n0 + 1 < N) yo[1] = static_cast<uint16_t>(o1);
+                if (n0 + 2 < N) yo[2] = static_cast<uint16_t>(o2);
+                if (n0 + 3 < N) yo[3] = static_cast<uint16_t>(o3);
+            }
+            if (acc_out) {
+                int32_t* ao = acc_out + o;
+                if (full && (reinterpret_cast<uintptr_t>(ao) & 15) == 0) {
+                    *reinterpret_cast<int4*>(ao) = t;
+                } else {
+                    ao[0] = t.x;
+                    if (n0 + 1 < N) ao[1] = t.y;
+                    if (n0 + 2 < N) ao[2] = t.z;
+                    if (n0 + 3 < N) ao[3] = t.w;
+                }
+            }
         }
     }
 }

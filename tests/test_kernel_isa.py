@@ -70,3 +70,27 @@ def test_mfma_operand_loads_issued_before_first_wait(mfma_asm):
         if weights != 4 * PS or acts != PS * MT:
             late.append((MT, PS, weights, acts))
     assert not late, f"(MT, PS, weight words, A operands before the first wait): {late}"
+
+
+def _meta(asm, name, key):
+    k = asm.index(".amdhsa_kernel " + name)
+    block = asm[k:asm.index(".end_amdhsa_kernel", k)]
+    return int(re.search(r"\." + key + r"\s+(\d+)", block).group(1))
+
+
+def test_no_scratch_and_declared_lds_only(gemv_asm, mfma_asm):
+    # No kernel spills to scratch, and each uses exactly the LDS it declares:
+    # a private array that the compiler moves into LDS (it does so for arrays
+    # indexed at run time) once made the MFMA kernel twice as slow.
+    for m in re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])E\S*):", gemv_asm, re.M):
+        name, fused = m.group(1), m.group(3) == "1"
+        assert _meta(gemv_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
+        # part_sh[16][64] + xsum_sh[16], + amax_sh[16] when fused (the
+        # activation row itself is dynamic LDS)
+        want = 16 * 64 * 4 + 16 * 4 + (16 * 4 if fused else 0)
+        assert _meta(gemv_asm, name, "amdhsa_group_segment_fixed_size") == want, name
+    for m in re.finditer(r"^(_ZN\S*gemm_mfma_kernelILi(\d+)ELi(\d+)E\S*):", mfma_asm, re.M):
+        name, MT = m.group(1), int(m.group(2))
+        assert _meta(mfma_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
+        # red[16 MT][68] int32 + inv_s_sh[16 MT] fp64 + s_sh[16 MT] fp32
+        assert _meta(mfma_asm, name, "amdhsa_group_segment_fixed_size") == 16 * MT * (68 * 4 + 8 + 4), name
