@@ -358,6 +358,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only")
+    ap.add_argument("--sections", default="fused,layer_set,batched,decode_step,torch",
+                    help="detail sections to run after the headline (comma list; for profiling one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--pmc-calibrate", action="store_true",
@@ -390,15 +392,19 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         detail["calibration_copy_bytes"] = 256 << 20
-    if not args.quick:
-        detail["fused_bf16_13824x2560"] = {}
+    sections = set() if args.quick else set(args.sections.split(","))
+    if "fused" in sections:
         fms = fused(bl, max(args.steps // 2, 100), min(args.warmup, 100))
         fb = gemv_bytes(1, 13824, 2560, 2, x_bytes=2)
         detail["fused_bf16_13824x2560"] = {"us": round(fms * 1e3, 3),
                                            "GBps": round(fb / (fms * 1e-3) / 1e9, 1)}
+    if "layer_set" in sections:
         detail["layer_set_int8"] = layer_shapes(bl, max(args.steps // 4, 100), 50)
+    if "batched" in sections:
         detail["batched_mfma"] = batched(bl, max(args.steps // 8, 50), 20)
+    if "decode_step" in sections:
         detail["decode_step_graph"] = decode_step(bl, 20)
+    if "torch" in sections:
         detail["torch_bf16_matmul_13824x2560"] = torch_bf16_context(200)
 
     traffic = pmc_traffic()

@@ -48,12 +48,12 @@ def _load():
     lib.oracle_quant_absmax_i8_bf16.argtypes = [P, I, I, P, P]
     lib.oracle_packed_bytes.argtypes = [I, I]
     lib.oracle_packed_bytes.restype = ctypes.c_size_t
-    lib.oracle_unpack_r64.argtypes = [P, I, I, P, P]
+    lib.oracle_unpack_tiles.argtypes = [P, I, I, P, P]
     lib.oracle_gemm_i32.argtypes = [P, P, I, I, I, P]
     lib.oracle_epilogue_bf16.argtypes = [P, P, P, I, I, I, P]
     lib.oracle_bitlinear_i8.argtypes = [P, P, P, P, I, I, I, I, P, P]
     lib.oracle_bitlinear_bf16.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
-    for name in ("oracle_quant_absmax_i8_f32", "oracle_quant_absmax_i8_bf16", "oracle_unpack_r64",
+    for name in ("oracle_quant_absmax_i8_f32", "oracle_quant_absmax_i8_bf16", "oracle_unpack_tiles",
                  "oracle_gemm_i32", "oracle_epilogue_bf16", "oracle_bitlinear_i8",
                  "oracle_bitlinear_bf16"):
         getattr(lib, name).restype = ctypes.c_int
@@ -127,7 +127,7 @@ def packed_bytes(N: int, K: int) -> int:
     return int(_load().oracle_packed_bytes(N, K))
 
 
-def unpack_r64(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+def unpack_tiles(packed: np.ndarray, N: int, K: int) -> np.ndarray:
     """Decode packed ternary weights (layout spelled out in oracle.c) to int8 N x K.
 
     Raises OracleError if a real position holds code 0 or a padding position
@@ -138,12 +138,12 @@ def unpack_r64(packed: np.ndarray, N: int, K: int) -> np.ndarray:
         raise OracleError(f"packed buffer has {p.size} bytes, expected {packed_bytes(N, K)}")
     w = np.empty((N, K), dtype=np.int8)
     bad = ctypes.c_int64(-1)
-    rc = _load().oracle_unpack_r64(_ptr(p), N, K, _ptr(w), ctypes.byref(bad))
+    rc = _load().oracle_unpack_tiles(_ptr(p), N, K, _ptr(w), ctypes.byref(bad))
     if rc == ERR_CODE:
         raise OracleError(f"code 0 at real position (flat index {bad.value})")
     if rc == ERR_PAD:
         raise OracleError(f"non-zero code in padding (byte {bad.value})")
-    _check(rc, "unpack_r64")
+    _check(rc, "unpack_tiles")
     return w
 
 

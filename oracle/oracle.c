@@ -14,12 +14,12 @@
  * What is computed, and where the pages define it:
  *   quant_absmax_i8  per-token absmax int8 activations, s = 127 / max|x|,
  *                    round, clamp to [-128, 127]                   [W2A8] §六 item 3
- *   unpack_r64       ternary weights stored as 2-bit codes w + 2, four per
+ *   unpack_tiles       ternary weights stored as 2-bit codes w + 2, four per
  *                    byte, the 16 codes of a 32-bit word interleaved so that
  *                    shift 2i + mask 0x03030303 yields elements 4i..4i+3
  *                                                                  [W2A8] §5.2
  *                    (the 16-row x 256-K tiling is this project's own layout;
- *                    its bit-level definition is restated at unpack_r64)
+ *                    its bit-level definition is restated at unpack_tiles)
  *   gemm_i32         int32 dot products of int8 activations and ternary
  *                    weights, exactly the int32 matmul the page's test uses
  *                                                                  [W2A8] §三 item 2, §5.3
@@ -224,7 +224,7 @@ static size_t layout_byte(size_t n, size_t k, size_t steps, int *bit)
  * Returns OR_OK, OR_ERR_CODE (and *bad = flat index n*K+k of the first bad
  * code) or OR_ERR_PAD (and *bad = byte offset of the first bad padding byte).
  */
-int oracle_unpack_r64(const uint8_t* packed, int N, int K, int8_t* w, int64_t* bad)
+int oracle_unpack_tiles(const uint8_t* packed, int N, int K, int8_t* w, int64_t* bad)
 {
     if (!packed || !w || N <= 0 || K <= 0)
         return OR_ERR_ARG;

@@ -53,7 +53,7 @@ def test_host_packer_round_trips_through_oracle_unpack(N, K):
     w = g.integers(-1, 2, size=(N, K), dtype=np.int8)
     packed, bad = bl.bl_pack_ternary_host(w)
     assert bad == 0
-    np.testing.assert_array_equal(oracle.unpack_r64(packed, N, K), w)
+    np.testing.assert_array_equal(oracle.unpack_tiles(packed, N, K), w)
 
 
 def test_host_packer_counts_invalid_entries():
@@ -63,7 +63,7 @@ def test_host_packer_counts_invalid_entries():
     packed, bad = bl.bl_pack_ternary_host(w)
     assert bad == 2
     with pytest.raises(oracle.OracleError, match="code 0"):
-        oracle.unpack_r64(packed, 16, 256)
+        oracle.unpack_tiles(packed, 16, 256)
 
 
 # Argument validation.  Non-null dummy addresses are fine: every call below

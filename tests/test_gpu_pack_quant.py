@@ -1,6 +1,6 @@
 """GPU parity of the weight packer and the activation quantiser against the oracle.
 
-Packer: the device bytes must decode (oracle.unpack_r64, written from the
+Packer: the device bytes must decode (oracle.unpack_tiles, written from the
 layout's bit-level definition) to exactly the input matrix, padding included,
 and equal the host twin byte for byte.  Quantiser: int8 values and fp32
 scales bit-exact against oracle.quant_absmax_i8 (W2A8 page §六 item 3).
@@ -34,7 +34,7 @@ def test_pack_matches_definition(bl, N, K):
     torch.cuda.synchronize()
     p = packed.cpu().numpy()
     assert int(bad.item()) == 0
-    np.testing.assert_array_equal(oracle.unpack_r64(p, N, K), w)
+    np.testing.assert_array_equal(oracle.unpack_tiles(p, N, K), w)
     host, nbad = bl.bl_pack_ternary_host(w)
     assert nbad == 0
     np.testing.assert_array_equal(p, host)

@@ -77,12 +77,12 @@ def _all_zero_tile():
 
 
 def test_hand_worked_tiled_bytes():
-    for line in read_golden("r64_examples.txt"):
+    for line in read_golden("tile_examples.txt"):
         n, k, v, off, byte = line.split()
         n, k, v, off, byte = int(n), int(k), int(v), int(off), int(byte, 16)
         p = _all_zero_tile()
         p[off] = byte
-        w = oracle.unpack_r64(p, 16, 256)
+        w = oracle.unpack_tiles(p, 16, 256)
         expect = np.zeros((16, 256), dtype=np.int8)
         expect[n, k] = v
         np.testing.assert_array_equal(w, expect)
@@ -94,7 +94,7 @@ def test_tiled_words_decode_the_page_way():
     N, K = 32, 512
     codes = g.integers(1, 4, size=(oracle.packed_bytes(N, K), 4)).astype(np.uint8)
     packed = (codes[:, 0] | codes[:, 1] << 2 | codes[:, 2] << 4 | codes[:, 3] << 6).astype(np.uint8)
-    w = oracle.unpack_r64(packed, N, K)
+    w = oracle.unpack_tiles(packed, N, K)
     words = packed.view("<u4")
     steps = K // 256
     for n in (0, 1, 5, 15, 16, 22, 31):
@@ -119,12 +119,12 @@ def test_padding_layout_and_errors():
             slot = 16 * ((n % 16) // 4) + (k % 256) // 16
             off = t * 1024 + 16 * slot + 4 * (n % 4) + e % 4
             p[off] |= 2 << (2 * (e // 4))
-    assert (oracle.unpack_r64(p, N, K) == 0).all()
+    assert (oracle.unpack_tiles(p, N, K) == 0).all()
     bad = p.copy()
     bad[0] &= 0xFC                      # w[0][0] becomes code 0
     with pytest.raises(oracle.OracleError, match="code 0"):
-        oracle.unpack_r64(bad, N, K)
+        oracle.unpack_tiles(bad, N, K)
     bad = p.copy()
     bad[-1] = 0x01                      # a padding row of the last tile gets a code
     with pytest.raises(oracle.OracleError, match="padding"):
-        oracle.unpack_r64(bad, N, K)
+        oracle.unpack_tiles(bad, N, K)
