@@ -53,7 +53,9 @@ def _load():
     lib.oracle_epilogue_bf16.argtypes = [P, P, P, I, I, I, P]
     lib.oracle_bitlinear_i8.argtypes = [P, P, P, P, I, I, I, I, P, P]
     lib.oracle_bitlinear_bf16.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
-    for name in ("oracle_quant_absmax_i8_f32", "oracle_quant_absmax_i8_bf16", "oracle_unpack_tiles",
+    lib.oracle_absmean_scales.argtypes = [ctypes.c_uint16, P, P]
+    lib.oracle_ternary_from_scale.argtypes = [P, ctypes.c_size_t, ctypes.c_uint16, P]
+    for name in ("oracle_absmean_scales", "oracle_ternary_from_scale", "oracle_quant_absmax_i8_f32", "oracle_quant_absmax_i8_bf16", "oracle_unpack_tiles",
                  "oracle_gemm_i32", "oracle_epilogue_bf16", "oracle_bitlinear_i8",
                  "oracle_bitlinear_bf16"):
         getattr(lib, name).restype = ctypes.c_int
@@ -223,3 +225,73 @@ def decode_step(nodes):
     Returns the list of (q, s, acc, y) per node, in node order.
     """
     return [bitlinear_bf16(x, w, ws, wn) for (x, w, ws, wn) in nodes]
+
+
+# --------------------------------------------------------------------------
+# Weight ternarisation by the mean absolute value  ([W2A8] §4.2)
+# --------------------------------------------------------------------------
+
+def bf16_rne_ratio(num: int, den: int) -> int:
+    """bf16 bits of num/den (num >= 0, den > 0) rounded to nearest, ties to even.
+
+    Exact integer arithmetic from the format's definition: around a value
+    whose leading bit is 2^E the spacing is 2^(E-7) (normal, E >= -126) or
+    2^-133 (below); the value divided by the spacing is rounded to an integer
+    r, and the encoding of r * 2^u is ((u + 133) << 7) + r, which carries into
+    the exponent when r reaches 256 and is +inf (0x7F80) from 2^128 on.
+    """
+    if num < 0 or den <= 0:
+        raise OracleError("bf16_rne_ratio needs num >= 0, den > 0")
+    if num == 0:
+        return 0
+    E = num.bit_length() - den.bit_length()        # num/den in [2^(E-1), 2^(E+1))
+    if (num << max(0, -E)) < (den << max(0, E)):
+        E -= 1                                     # now 2^E <= num/den < 2^(E+1)
+    u = E - 7 if E >= -126 else -133
+    a, b = (num, den << u) if u >= 0 else (num << -u, den)
+    r, rem = divmod(a, b)
+    if 2 * rem > b or (2 * rem == b and r & 1):
+        r += 1
+    return min(((u + 133) << 7) + r, 0x7F80)
+
+
+def absmean_bf16(w_bits) -> int:
+    """bf16 bits of the exact mean of |w| over bf16 weights (given as uint16 bit patterns).
+
+    |w| = m * 2^(E' - 134) with E' = max(E, 1) and m = f + 128 [E >= 1] (E the
+    exponent field, f the fraction); the mantissas are summed per exponent
+    (exact in float64: at most 255 * 2^44 < 2^53), the per-exponent sums are
+    combined as Python integers, and the mean is rounded once.
+    """
+    b = np.asarray(w_bits, dtype=np.uint16).reshape(-1).astype(np.int64) & 0x7FFF
+    if b.size == 0:
+        raise OracleError("empty weight matrix")
+    if np.any(b >= 0x7F80):
+        raise OracleError("weights must be finite")
+    E = b >> 7
+    m = (b & 0x7F) + np.where(E >= 1, 128, 0)
+    Ep = np.maximum(E, 1)
+    per_exp = np.bincount(Ep, weights=m.astype(np.float64), minlength=256)
+    total = 0                                      # sum of |w|, in units of 2^-133
+    for e in range(1, 256):
+        if per_exp[e]:
+            total += int(per_exp[e]) << (e - 1)
+    return bf16_rne_ratio(total, b.size << 133)
+
+
+def ternarize_absmean(w_bits):
+    """Ternarise bf16 weights (uint16 bit patterns, N x K) as the page's converter does.
+
+    Returns (q int8 N x K in {-1, 0, 1}, mean_bits, s_bits, ws_bits): the bf16
+    mean of |W|, the bf16 multiplier s = 1 / max(mean, 1e-5), and the bf16
+    weight scale ws = 1 / s that goes with the ternary matrix.
+    """
+    w = _c(np.atleast_2d(w_bits), np.uint16)
+    mean = absmean_bf16(w)
+    s_b = ctypes.c_uint16()
+    ws_b = ctypes.c_uint16()
+    lib = _load()
+    _check(lib.oracle_absmean_scales(mean, ctypes.byref(s_b), ctypes.byref(ws_b)), "absmean_scales")
+    q = np.empty(w.shape, dtype=np.int8)
+    _check(lib.oracle_ternary_from_scale(_ptr(w), w.size, s_b.value, _ptr(q)), "ternary_from_scale")
+    return q, mean, int(s_b.value), int(ws_b.value)

@@ -25,6 +25,9 @@
  *                                                                  [W2A8] §三 item 2, §5.3
  *   epilogue_bf16    rescale by the weight scale of the output's N-segment
  *                    and by the activation scale, round to bf16     [W2A8] §5.3
+ *   absmean_scales,  ternarise a bf16 weight matrix by its mean absolute
+ *   ternary_from_scale  value: s = 1/mean, Wt = clamp(round(W*s), -1, 1),
+ *                    ws = 1/s, in the page's bf16 arithmetic       [W2A8] §4.2
  *
  * Readings where the page is ambiguous (each one is listed with its reason in
  * the design notes):
@@ -337,4 +340,66 @@ int oracle_bitlinear_bf16(const uint16_t* x, const int8_t* w, const uint16_t* ws
     if (rc != OR_OK)
         return rc;
     return oracle_bitlinear_i8(q, w, s, ws, ws_num, M, N, K, acc, y);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Weight ternarisation by the mean absolute value  ([W2A8] §4.2)           */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * The page's converter quantises each projection matrix W (bf16) on its own:
+ *     s  = 1 / max(mean|W|, 1e-5)
+ *     Wt = clamp(round(W * s), -1, 1)          stored as int8, then packed
+ *     ws = 1 / s                               the matrix's weight scale
+ * written as torch operations on bf16 tensors.  Such an operation computes in
+ * fp32 and rounds its result to bf16 (nearest, ties to even); that is the
+ * arithmetic followed here, step by step.  Readings:
+ *   - mean|W| is the exact mean of the bf16 magnitudes, rounded once to bf16
+ *     (torch accumulates in fp32 in an unspecified order; the exact mean is
+ *     the order-free value it approximates).  It is passed in as mean_bits,
+ *     computed by the Python side (exact integer arithmetic);
+ *   - the clamp compares in fp32 with 1e-5f and stores bf16(1e-5f) below it;
+ *   - round is round half to even; W must be finite.
+ */
+
+/* bf16 of an fp32 value, via the fp64 rounding above (fp32 -> fp64 is exact). */
+static uint16_t bf16_of_float(float f)
+{
+    return oracle_bf16_rne((double)f);
+}
+
+/* From the bf16 mean: the multiplier s and the weight scale ws (both bf16). */
+int oracle_absmean_scales(uint16_t mean_bits, uint16_t* s_bits, uint16_t* ws_bits)
+{
+    if (!s_bits || !ws_bits)
+        return OR_ERR_ARG;
+    float mean = bf16_bits_to_float(mean_bits);
+    if (!(mean >= 0.0f) || isinf(mean))
+        return OR_ERR_ARG;
+    if (mean < 1e-5f)
+        mean = bf16_bits_to_float(bf16_of_float(1e-5f));
+    uint16_t s = bf16_of_float(1.0f / mean);             /* one fp32 division */
+    uint16_t ws = bf16_of_float(1.0f / bf16_bits_to_float(s));
+    *s_bits = s;
+    *ws_bits = ws;
+    return OR_OK;
+}
+
+/* Wt[i] = clamp(round(bf16(W[i] * s)), -1, 1) for n bf16 weights. */
+int oracle_ternary_from_scale(const uint16_t* w, size_t n, uint16_t s_bits, int8_t* q)
+{
+    if ((!w || !q) && n)
+        return OR_ERR_ARG;
+    float s = bf16_bits_to_float(s_bits);
+    for (size_t i = 0; i < n; ++i) {
+        float prod = bf16_bits_to_float(w[i]) * s;       /* exact: 8 x 8 significant bits */
+        float t = bf16_bits_to_float(bf16_of_float(prod));
+        float r = nearbyintf(t);                         /* ties to even */
+        if (r > 1.0f)
+            r = 1.0f;
+        if (r < -1.0f)
+            r = -1.0f;
+        q[i] = (int8_t)r;
+    }
+    return OR_OK;
 }
