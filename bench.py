@@ -216,6 +216,31 @@ def batched(bl, steps, warmup):
     return out
 
 
+def ternarize(bl, steps, warmup):
+    """Weight ternarisation + packing of a bf16 13824 x 2560 matrix ([W2A8] §4.2): one call
+    = exponent histogram, finalise, ternarise-and-pack.  Four rotating weight copies (283 MB)."""
+    torch = _torch()
+    N, K = 13824, 2560
+    g = synth.rng(synth.seed_for(9, 1, 0))
+    w = bf16_dev(synth.weights_bf16(g, N, K))
+    copies = [w] + [w.clone() for _ in range(3)]
+    packed = torch.empty(bl.bl_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(3, dtype=torch.bfloat16, device="cuda")
+    work = torch.empty(bl.TERNARIZE_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    lib = bl.lib()
+
+    def launch(i):
+        rc = lib.ternarize_weights_absmean(copies[i % 4].data_ptr(), packed.data_ptr(),
+                                           scales.data_ptr(), work.data_ptr(), N, K,
+                                           torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"ternarize_weights_absmean failed: {rc}")
+
+    ms = time_graph(launch, steps, warmup)
+    b = 2 * (2 * N * K) + N * K // 4 + 2048 + 6   # bf16 read twice, packed written
+    return {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": b}
+
+
 def decode_step(bl, reps):
     """30 layers x {qkv, o, gate+up, down}, fused quantisation, one bl_graph per step."""
     torch = _torch()
@@ -358,7 +383,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only")
-    ap.add_argument("--sections", default="fused,layer_set,batched,decode_step,torch",
+    ap.add_argument("--sections", default="fused,layer_set,batched,decode_step,ternarize,torch",
                     help="detail sections to run after the headline (comma list; for profiling one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -404,6 +429,8 @@ def main():
         detail["batched_mfma"] = batched(bl, max(args.steps // 8, 50), 20)
     if "decode_step" in sections:
         detail["decode_step_graph"] = decode_step(bl, 20)
+    if "ternarize" in sections:
+        detail["ternarize_pack_bf16_13824x2560"] = ternarize(bl, 50, 10)
     if "torch" in sections:
         detail["torch_bf16_matmul_13824x2560"] = torch_bf16_context(200)
 

@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
 BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP, BL_ERR_ARG = 0, -1, -2, -3, -4, -5
+TERNARIZE_WORKSPACE_BYTES = 2048   # BL_TERNARIZE_WORKSPACE_BYTES
 # Largest K the single-kernel M = 1 paths take (include/bitlinear.h); beyond it the
 # bf16 entry needs staging buffers for the quantised activations.
 GEMV_MAX_K = 61440
@@ -30,6 +31,7 @@ SIGNATURES = {
     "bl_packed_bytes": (ctypes.c_size_t, [_I, _I]),
     "pack_ternary_weights": (_I, [_P, _P, _I, _I, _P, _P]),
     "bl_pack_ternary_host": (ctypes.c_int64, [_P, _P, _I, _I]),
+    "ternarize_weights_absmean": (_I, [_P, _P, _P, _P, _I, _I, _P]),
     "quantize_act_absmax_i8": (_I, [_P, _I, _P, _P, _I, _I, _P]),
     "bitlinear_i8xi2": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _P]),
     "bitlinear_bf16_i8xi2": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P]),
@@ -127,6 +129,24 @@ def bl_pack_ternary_host(w: np.ndarray):
     if r < 0:
         raise BitLinearError(int(r), "bl_pack_ternary_host")
     return out, int(r)
+
+
+def ternarize_weights_absmean(w, workspace=None):
+    """bf16 N x K weights (device) -> (packed uint8, scales bf16[3] = ws, s, mean).
+
+    Ternarises by the mean absolute value and packs (include/bitlinear.h);
+    ``workspace`` (uint8, TERNARIZE_WORKSPACE_BYTES) is allocated when not given.
+    """
+    import torch
+    _require(w, torch.bfloat16, "w")
+    N, K = w.shape
+    packed = torch.empty(bl_packed_bytes(N, K), dtype=torch.uint8, device=w.device)
+    scales = torch.empty(3, dtype=torch.bfloat16, device=w.device)
+    if workspace is None:
+        workspace = torch.empty(TERNARIZE_WORKSPACE_BYTES, dtype=torch.uint8, device=w.device)
+    _check(lib().ternarize_weights_absmean(_ptr(w), _ptr(packed), _ptr(scales), _ptr(workspace),
+                                           N, K, _stream()), "ternarize_weights_absmean")
+    return packed, scales
 
 
 def quantize_act_absmax_i8(x):

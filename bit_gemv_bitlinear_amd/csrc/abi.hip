@@ -123,6 +123,17 @@ int64_t bl_pack_ternary_host(const int8_t* w_host, uint8_t* packed_host, int N, 
     return bl::pack_host(w_host, packed_host, N, K);
 }
 
+int ternarize_weights_absmean(const uint16_t* w, uint8_t* packed, uint16_t* scales,
+                              void* workspace, int N, int K, hipStream_t stream) {
+    if (!w || !packed || !scales || !workspace) return BL_ERR_NULL;
+    const int rc = check_mnk(1, N, K);
+    if (rc) return rc;
+    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(workspace, 8))
+        return BL_ERR_ALIGN;
+    (void)hipGetLastError();
+    return status_of(bl::launch_ternarize(w, packed, scales, workspace, N, K, stream));
+}
+
 int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int M, int K,
                            hipStream_t stream) {
     if (!x || !q || !s) return BL_ERR_NULL;

@@ -44,6 +44,11 @@ hipError_t launch_gemv_bf16_fused(const uint16_t* x, const uint8_t* packed, cons
                                   int ws_num, uint16_t* y, int8_t* q_out, float* s_out,
                                   int32_t* acc, int N, int K, hipStream_t stream);
 
+// Ternarise a bf16 N x K matrix by its mean |w| and pack it; scales[0..2] =
+// ws, s, mean (bf16); workspace: 256 uint64 (the exponent histogram).
+hipError_t launch_ternarize(const uint16_t* w, uint8_t* packed, uint16_t* scales,
+                            void* workspace, int N, int K, hipStream_t stream);
+
 // M >= 2, int8 activations, int8 MFMA.
 hipError_t launch_gemm_mfma(const int8_t* xq, const uint8_t* packed, const float* s,
                             const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int M,

@@ -1,4 +1,4 @@
-// pack.hip -- packing of ternary weights into the 64x64-tile layout.
+// pack.hip -- packing of ternary weights into the 16x256-tile layout.
 //
 // Source page: "BitNet GPU 推理框架：从零构建 W2A8 的 2-bit 大模型 CUDA GEMV 内核"
 // (blog.gitcode.com), §5.2: each weight w in {-1, 0, 1} becomes the code

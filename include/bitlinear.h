@@ -113,6 +113,37 @@ int pack_ternary_weights(const int8_t* w, uint8_t* packed, int N, int K,
  */
 int64_t bl_pack_ternary_host(const int8_t* w_host, uint8_t* packed_host, int N, int K);
 
+/* Bytes of device workspace ternarize_weights_absmean needs (8-byte aligned). */
+#define BL_TERNARIZE_WORKSPACE_BYTES 2048
+
+/*
+ * ternarize_weights_absmean -- ternarise a bf16 weight matrix by its mean
+ * absolute value and pack it ([W2A8] §4.2, then §5.1-5.2):
+ *   mean = bf16(exact mean of |w| over all N*K entries)
+ *   s    = bf16(fl32(1 / max(mean, 1e-5)))      (below 1e-5: bf16(1e-5f))
+ *   Wt   = clamp(round_half_even(bf16(fl32(w * s))), -1, 1)
+ *   ws   = bf16(fl32(1 / s))                    the matrix's weight scale
+ * i.e. the page's converter in torch bf16 arithmetic (each operation in fp32,
+ * rounded to bf16, ties to even), with the mean taken exactly rather than in
+ * an order-dependent fp32 sum.  Wt is written packed, as pack_ternary_weights
+ * would pack it.
+ *   w          device, bf16, N x K row-major, finite values, 16-byte aligned
+ *   packed     device, bl_packed_bytes(N, K) bytes, written in full
+ *   scales     device, bf16[3]: scales[0] = ws, scales[1] = s, scales[2] =
+ *              mean (before the floor); ws is what bitlinear_* take
+ *   workspace  device, BL_TERNARIZE_WORKSPACE_BYTES, 8-byte aligned, owned by
+ *              the caller; its contents need no initialisation; calls that
+ *              share one workspace must not overlap
+ * N and K as for the layer (K % 16 == 0, K <= 2^20, N <= 2^24).  Several
+ * matrices meant to share one packed buffer (e.g. w1 and w3 of a fused
+ * gate+up with ws_num = 2) are ternarised one by one; when the first has a
+ * multiple of 16 rows, their packed buffers concatenate to the packing of the
+ * stacked matrix.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP.
+ */
+int ternarize_weights_absmean(const uint16_t* w, uint8_t* packed, uint16_t* scales,
+                              void* workspace, int N, int K, hipStream_t stream);
+
 /*
  * quantize_act_absmax_i8 -- per-token (per-row) absmax int8 quantisation
  * ([W2A8] §六 item 3):

@@ -392,7 +392,8 @@ int oracle_ternary_from_scale(const uint16_t* w, size_t n, uint16_t s_bits, int8
         return OR_ERR_ARG;
     float s = bf16_bits_to_float(s_bits);
     for (size_t i = 0; i < n; ++i) {
-        float prod = bf16_bits_to_float(w[i]) * s;       /* exact: 8 x 8 significant bits */
+        /* fl32(w * s): exact (8 x 8 significant bits) unless it underflows */
+        float prod = bf16_bits_to_float(w[i]) * s;
         float t = bf16_bits_to_float(bf16_of_float(prod));
         float r = nearbyintf(t);                         /* ties to even */
         if (r > 1.0f)

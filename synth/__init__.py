@@ -73,6 +73,12 @@ def _top16(f: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(f, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
+def weights_bf16(g, N, K, sigma=0.02):
+    """bf16 weight matrix (uint16 bit patterns): N(0, sigma^2) draws, fp32 cut to its top 16 bits."""
+    v = (g.standard_normal((N, K)) * sigma).astype(np.float32)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
 def normal_bf16_bits(g: np.random.Generator, M: int, K: int) -> np.ndarray:
     """x ~ N(0, 1) on the bf16 grid (fp32 draw, top 16 bits kept), as uint16 bit patterns."""
     return _top16(normal_f32(g, M, K))

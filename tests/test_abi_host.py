@@ -125,6 +125,19 @@ def test_quantize_and_pack_errors():
     assert p(A, A + 4, 64, 64, None, None) == bl.BL_ERR_ALIGN
 
 
+def test_ternarize_errors():
+    t = bl.lib().ternarize_weights_absmean
+    assert t(None, A, A, A, 64, 64, None) == bl.BL_ERR_NULL
+    assert t(A, A, A, None, 64, 64, None) == bl.BL_ERR_NULL
+    assert t(A, A, A, A, 0, 64, None) == bl.BL_ERR_SHAPE
+    assert t(A, A, A, A, 64, 40, None) == bl.BL_ERR_SHAPE         # K % 16 != 0
+    assert t(A, A, A, A, 64, (1 << 20) + 16, None) == bl.BL_ERR_SHAPE
+    assert t(A + 8, A, A, A, 64, 64, None) == bl.BL_ERR_ALIGN      # w must be 16-byte aligned
+    assert t(A, A, U, A, 64, 64, None) == bl.BL_ERR_ALIGN
+    assert t(A, A, A, A + 4, 64, 64, None) == bl.BL_ERR_ALIGN
+    assert bl.TERNARIZE_WORKSPACE_BYTES == 2048
+
+
 def test_graph_errors():
     g = ctypes.c_void_p()
     lib = bl.lib()

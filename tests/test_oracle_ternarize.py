@@ -128,3 +128,16 @@ def test_matches_the_pages_torch_code_where_its_sum_is_exact():
         q, mean, s, ws = oracle.ternarize_absmean(b)
         np.testing.assert_array_equal(q, wt.numpy())
         assert ws == int(ws_t.view(torch.int16).numpy()[0]) & 0xFFFF
+
+
+def test_mean_exactly_on_a_tie_and_one_subnormal_above():
+    # 256 entries summing to 257 plus 256 zeros: mean = 0.5 * (1 + 2^-8), a bf16
+    # tie that rounds to even 0.5; one zero raised to 2^-133 puts the mean just
+    # above it (rounds up to 0.5 + 2^-8).  Only an exact sum sees the difference.
+    v = np.zeros(512, dtype=np.float32)
+    v[0:512:2][:255] = 1.0
+    v[510] = 2.0
+    b = bits_of(v).reshape(16, 32)
+    assert oracle.absmean_bf16(b) == 0x3F00
+    b[0, 1] = 0x0001
+    assert oracle.absmean_bf16(b) == 0x3F01
