@@ -52,7 +52,15 @@ namespace bl {
 namespace {
 
 constexpr int kMaxWaves = 16;
-constexpr int kCached = 2;   // 16-byte activation chunks per thread kept in registers
+// C = 16-byte activation chunks per thread loaded ahead of the weights and
+// kept in registers (1, 2 or 4, a template argument chosen per shape).
+// Chunks beyond them are loaded after the weights, and since the waits count
+// loads in issue order, using them waits for every weight; so C covers the
+// row wherever it can (bf16 rows have twice the chunks of int8 rows: 2560 x
+// 2 B over 128 threads for qkv and o, 6912 x 2 B over 256 threads for down).
+// Chunks a thread does not need cost code on the path to the main loop, so C
+// is no larger than the row needs.
+constexpr int kMaxCached = 4;
 
 struct RowAcc {
     int a1[4], a4[4], a16[4];
@@ -135,7 +143,7 @@ __device__ __forceinline__ int sum_i8x4(uint32_t d, int acc) {
 // FUSED = false: xin is int8 activations with scale s_in[0].
 // FUSED = true:  xin is bf16; the workgroup quantises it (per-token absmax,
 //                [W2A8] §六 item 3); workgroup 0 writes q_out / s_out if given.
-template <int P, bool FUSED>
+template <int P, bool FUSED, int C>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     const void* __restrict__ xin, const v4u* __restrict__ packed, const float* __restrict__ s_in,
     const uint16_t* __restrict__ ws, uint32_t seg_mul, int seg_shift, uint16_t* __restrict__ y,
@@ -165,6 +173,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     const uint32_t n_ws = static_cast<uint32_t>(min(n_out, N - 1));
     // unconditional: no branch, no early wait
     const uint16_t wsb = ws[(static_cast<uint64_t>(n_ws) * seg_mul) >> seg_shift];
+    constexpr int kCached = C;
     uint4 xv[kCached];
     const int n_in = FUSED ? (K >> 3) : n16;   // 16-byte input chunks
     const uint4* x16 = reinterpret_cast<const uint4*>(xin);
@@ -287,15 +296,21 @@ constexpr int kTargetSteps = 9;     // K steps per wavefront aimed at
 using GemvFn = void (*)(const void*, const v4u*, const float*, const uint16_t*, uint32_t, int,
                         uint16_t*, int32_t*, int8_t*, float*, int, int, int, int);
 
-template <bool FUSED, int... Ps>
+template <bool FUSED, int C, int... Ps>
 constexpr std::array<GemvFn, sizeof...(Ps)> kernel_table(std::integer_sequence<int, Ps...>) {
-    return {{&gemv_kernel<Ps + 1, FUSED>...}};
+    return {{&gemv_kernel<Ps + 1, FUSED, C>...}};
 }
 
-const std::array<GemvFn, kMaxSteps> kI8Kernels =
-    kernel_table<false>(std::make_integer_sequence<int, kMaxSteps>{});
-const std::array<GemvFn, kMaxSteps> kBf16Kernels =
-    kernel_table<true>(std::make_integer_sequence<int, kMaxSteps>{});
+using KernelRow = std::array<GemvFn, kMaxSteps>;
+// [fused][log2 C][P - 1]
+const std::array<std::array<KernelRow, 3>, 2> kKernels = {{
+    {{kernel_table<false, 1>(std::make_integer_sequence<int, kMaxSteps>{}),
+      kernel_table<false, 2>(std::make_integer_sequence<int, kMaxSteps>{}),
+      kernel_table<false, 4>(std::make_integer_sequence<int, kMaxSteps>{})}},
+    {{kernel_table<true, 1>(std::make_integer_sequence<int, kMaxSteps>{}),
+      kernel_table<true, 2>(std::make_integer_sequence<int, kMaxSteps>{}),
+      kernel_table<true, 4>(std::make_integer_sequence<int, kMaxSteps>{})}},
+}};
 
 hipError_t launch(bool fused, const void* x, const uint8_t* packed, const float* s,
                   const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int8_t* q_out,
@@ -308,7 +323,12 @@ hipError_t launch(bool fused, const void* x, const uint8_t* packed, const float*
     int lw = 0;
     while ((1 << lw) < wb) ++lw;
     const size_t lds = static_cast<size_t>(wb) * g.steps * kTileK;
-    const GemvFn fn = fused ? kBf16Kernels[g.steps - 1] : kI8Kernels[g.steps - 1];
+    // chunks of the activation row per thread, rounded up to 1, 2 or 4
+    const int chunks = fused ? K / 8 : K / 16;
+    const int threads = g.waves * 64;
+    const int need = (chunks + threads - 1) / threads;
+    const int lc = need <= 1 ? 0 : need <= 2 ? 1 : 2;
+    const GemvFn fn = kKernels[fused ? 1 : 0][lc][g.steps - 1];
     uint32_t seg_mul;
     int seg_shift;
     seg_divisor(N / ws_num, seg_mul, seg_shift);

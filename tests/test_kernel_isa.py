@@ -1,6 +1,6 @@
 """Structure of the compiled kernels (host-only: hipcc cross-compiles gfx950).
 
-Every gemv_kernel<P, FUSED> must issue all P of a wavefront's weight loads
+Every gemv_kernel<P, FUSED, C> must issue all P of a wavefront's weight loads
 (the non-temporal 16-byte loads) before its first wait on vector memory, and
 every gemm_mfma_kernel<MT, PS> all 4 * PS of its weight words (non-temporal
 4-byte loads) and all PS * MT of its activation operands: the waits count
@@ -42,8 +42,8 @@ def mfma_asm(tmp_path_factory):
 
 
 def test_weight_loads_issued_before_first_wait(gemv_asm):
-    kernels = list(re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])E\S*):", gemv_asm, re.M))
-    assert len(kernels) == 40   # P = 1..20, int8 and bf16 input
+    kernels = list(re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])ELi(\d)E\S*):", gemv_asm, re.M))
+    assert len(kernels) == 120   # P = 1..20, int8 and bf16 input, C = 1, 2, 4 cached chunks
     late = []
     for m in kernels:
         P = int(m.group(2))
@@ -82,7 +82,7 @@ def test_no_scratch_and_declared_lds_only(gemv_asm, mfma_asm):
     # No kernel spills to scratch, and each uses exactly the LDS it declares:
     # a private array that the compiler moves into LDS (it does so for arrays
     # indexed at run time) once made the MFMA kernel twice as slow.
-    for m in re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])E\S*):", gemv_asm, re.M):
+    for m in re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])ELi(\d)E\S*):", gemv_asm, re.M):
         name, fused = m.group(1), m.group(3) == "1"
         assert _meta(gemv_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
         # part_sh[16][64] + xsum_sh[16], + amax_sh[16] when fused (the
