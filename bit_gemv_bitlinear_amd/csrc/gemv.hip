@@ -291,7 +291,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
 
 constexpr int kMaxSteps = 20;
 constexpr int kMinGroups = 200;     // workgroups wanted in flight (256 CUs)
-constexpr int kTargetSteps = 9;     // K steps per wavefront aimed at
+// K steps per wavefront aimed at.  A narrow matrix (fewer than kNarrowBands
+// bands: fewer single-band workgroups than about 1.5 per CU) leaves most
+// SIMDs with one wavefront, whose dot products after the last tile arrives
+// set the tail, so it takes shorter runs.  Measured same-box: at 2560 x 2560,
+// 3840 x 2560 and 2560 x 6912 the shorter runs gain 0.05-0.27 us; at
+// 13824 x 2560 they lose 0.5 us.
+constexpr int kTargetSteps = 9;
+constexpr int kTargetStepsNarrow = 4;
+constexpr int kNarrowBands = 400;
 
 using GemvFn = void (*)(const void*, const v4u*, const float*, const uint16_t*, uint32_t, int,
                         uint16_t*, int32_t*, int8_t*, float*, int, int, int, int);
@@ -357,9 +365,10 @@ GemvShape gemv_shape(int N, int K) {
     const int S = (K + kTileK - 1) / kTileK;
     const int nbands = (N + kTileRows - 1) / kTileRows;
     // Wavefronts per band: the smallest power of two (the kernel splits by
-    // shifts) that leaves at most kTargetSteps steps per wavefront.
+    // shifts) that leaves at most the target number of steps per wavefront.
+    const int target = nbands < kNarrowBands ? kTargetStepsNarrow : kTargetSteps;
     int Wb = 1;
-    while (Wb < kMaxWaves && (S + Wb - 1) / Wb > kTargetSteps) Wb <<= 1;
+    while (Wb < kMaxWaves && (S + Wb - 1) / Wb > target) Wb <<= 1;
     const int P = (S + Wb - 1) / Wb;
     if (P > kMaxSteps) return GemvShape{0, 0, 0};
     // Bands per workgroup: as many as keep >= kMinGroups workgroups in flight.
