@@ -1,7 +1,8 @@
 """Structure of the compiled kernels (host-only: hipcc cross-compiles gfx950).
 
-Every gemv_kernel<P, FUSED, C> must issue all P of a wavefront's weight loads
-(the non-temporal 16-byte loads) before its first wait on vector memory, and
+Every gemv_kernel<P, FUSED, C> and gemv_local_kernel<P> must issue all P of
+a wavefront's weight loads (the non-temporal 16-byte loads) before its first
+wait on vector memory, and
 every gemm_mfma_kernel<MT, PS> all 4 * PS of its weight words (non-temporal
 4-byte loads) and all PS * MT of its activation operands: the waits count
 loads in issue order, so a load issued after the first wait is held back by
@@ -55,6 +56,21 @@ def test_weight_loads_issued_before_first_wait(gemv_asm):
     assert not late, f"(P, fused, weight loads before the first wait): {late}"
 
 
+def test_local_weight_loads_issued_before_first_wait(gemv_asm):
+    kernels = list(re.finditer(r"^(_ZN\S*gemv_local_kernelILi(\d+)E\S*):", gemv_asm, re.M))
+    assert sorted(int(m.group(2)) for m in kernels) == list(range(1, 13))
+    late = []
+    for m in kernels:
+        P = int(m.group(2))
+        body = gemv_asm[m.end():gemv_asm.index("s_endpgm", m.end())]
+        first_wait = body.index("s_waitcnt vmcnt")
+        weights = len(re.findall(r"global_load_dwordx4 [^\n]* nt\b", body[:first_wait]))
+        acts = len(re.findall(r"global_load_dwordx2 ", body[:first_wait]))
+        if weights != P or acts != P:
+            late.append((P, weights, acts))
+    assert not late, f"(P, weight loads, activation loads before the first wait): {late}"
+
+
 def test_mfma_operand_loads_issued_before_first_wait(mfma_asm):
     kernels = list(re.finditer(r"^(_ZN\S*gemm_mfma_kernelILi(\d+)ELi(\d+)E\S*):", mfma_asm, re.M))
     # MT = 1..4 m tiles, PS = 1..min(16, 20 / MT) steps
@@ -89,6 +105,11 @@ def test_no_scratch_and_declared_lds_only(gemv_asm, mfma_asm):
         # activation row itself is dynamic LDS)
         want = 16 * 64 * 4 + 16 * 4 + (16 * 4 if fused else 0)
         assert _meta(gemv_asm, name, "amdhsa_group_segment_fixed_size") == want, name
+    for m in re.finditer(r"^(_ZN\S*gemv_local_kernelILi(\d+)E\S*):", gemv_asm, re.M):
+        name = m.group(1)
+        assert _meta(gemv_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
+        # part_sh[16][64] + amax_sh[16] (the quantised words are dynamic LDS)
+        assert _meta(gemv_asm, name, "amdhsa_group_segment_fixed_size") == 16 * 64 * 4 + 16 * 4, name
     for m in re.finditer(r"^(_ZN\S*gemm_mfma_kernelILi(\d+)ELi(\d+)E\S*):", mfma_asm, re.M):
         name, MT = m.group(1), int(m.group(2))
         assert _meta(mfma_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
