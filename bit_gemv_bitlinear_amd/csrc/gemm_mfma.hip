@@ -21,10 +21,11 @@
 //   * all PS x 4 weight words of a chunk are loaded up front (PS is a
 //     template argument, so the loads are unconditional: steps past the end
 //     re-read the last step and add zero), and so are the
-//     chunk's PS x MT A operands (16 rows m x 64 K, 16 bytes per lane
-//     straight from the int8 activations, zero outside M and K): both come
-//     from far enough away that only loads issued together hide their
-//     latency (PS * MT <= 20 bounds the registers);
+//     chunk's PS x MT A operands (16 rows m x 64 K, 16 bytes per lane from
+//     the int8 activations, loaded four lanes to a row and moved into the
+//     operand layout through LDS): both come from far enough away that only
+//     loads issued together hide their latency (PS * MT <= 20 bounds the
+//     registers);
 //   * the wavefronts' int32 tiles are added with LDS atomics (exact in any
 //     order), then the epilogue writes bf16 through the division-free fp64
 //     rounding (and optionally int32).
@@ -55,16 +56,17 @@ __device__ __forceinline__ v4i decode_b(uint32_t w) {
     return b;
 }
 
-// A operands of one 64-K step for MT m tiles: 16 bytes of row m at K offset
-// 64*st + 16*g, from clamped addresses so that the loads are unconditional.
+// A operands of one 64-K step for MT m tiles, as loaded: 16 bytes of each m
+// tile's row (this lane's row) at K offset 64*st + 16*chunk, from clamped
+// addresses so that the loads are unconditional.
 // Nothing needs zeroing: a row m >= M (read as row M - 1) only reaches its
 // own outputs, which are not written; K positions >= K in the last step
 // meet padding codes, which decode to 0; whole steps past the end are
 // zeroed where they are used.
 template <int MT>
-__device__ __forceinline__ void load_a(const int8_t* const (&row)[MT], int st, int g, int K,
+__device__ __forceinline__ void load_a(const int8_t* const (&row)[MT], int st, int chunk, int K,
                                        v4i (&a)[MT]) {
-    const int kc = min(st * 64 + 16 * g, K - 16);
+    const int kc = min(st * 64 + 16 * chunk, K - 16);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) a[mt] = *reinterpret_cast<const v4i*>(row[mt] + kc);
 }
@@ -79,6 +81,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
     __shared__ __align__(16) int red[MT * 16][kRedPitch];
     __shared__ double inv_s_sh[MT * 16];
     __shared__ float s_sh[MT * 16];
+    __shared__ __align__(16) v4i stage_sh[kMfmaMaxWaves][MT * 64];
     const int nthreads = blockDim.x;
     const int nwaves = nthreads >> 6;
     const int tid = threadIdx.x;
@@ -97,11 +100,31 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
     // the activation scale of m row tid (if any) is loaded now and inverted
     // after the main loop, so that neither waits in front of the weight loads
     const float s_row = s[min(m0 + min(tid, MT * 16 - 1), M - 1)];
+    // The epilogue's weight scales: this thread writes columns n0 .. n0 + 3
+    // of its rows (fixed per thread, the row stride being a multiple of 16),
+    // loaded now so that no load is left to wait on after the main loop.
+    const int c4 = (tid & 15) * 4;
+    const int n0 = col * 64 + c4;
+    uint16_t wsb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        wsb[e] = ws[(static_cast<uint64_t>(min(n0 + e, N - 1)) * seg_mul) >> seg_shift];
 
+    // A operands are loaded four lanes to a row -- lane 4q + i takes row q
+    // of each m tile, 16-byte chunk (i + q/2) % 4 of the step, so that a quad
+    // reads 64 contiguous bytes of one line (loaded in the operand layout,
+    // four lanes of a quad would touch four rows, which costs the memory
+    // pipeline several times as much) -- and moved into the operand layout
+    // (lane (j, g): row j, chunk g) through the wavefront's LDS slots; the
+    // skew makes those LDS reads free of bank conflicts.
+    const int a_row = lane >> 2;
+    const int a_chunk = ((lane & 3) + (lane >> 3)) & 3;
+    const int rd_slot = 4 * j + ((g - (j >> 1)) & 3);   // where lane (j, g)'s operand lands
+    v4i* const stage = stage_sh[wave];
     const int8_t* row[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-        row[mt] = xq + static_cast<size_t>(min(m0 + 16 * mt + j, M - 1)) * K;
+        row[mt] = xq + static_cast<size_t>(min(m0 + 16 * mt + a_row, M - 1)) * K;
     size_t band_base[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -125,7 +148,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
         v4i a[PS][MT];
         if constexpr (kAFirst) {
 #pragma unroll
-            for (int p = 0; p < PS; ++p) load_a<MT>(row, base + p, g, K, a[p]);
+            for (int p = 0; p < PS; ++p) load_a<MT>(row, base + p, a_chunk, K, a[p]);
         }
         uint32_t bw[PS][4];
 #pragma unroll
@@ -139,7 +162,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
         }
         if constexpr (!kAFirst) {
 #pragma unroll
-            for (int p = 0; p < PS; ++p) load_a<MT>(row, base + p, g, K, a[p]);
+            for (int p = 0; p < PS; ++p) load_a<MT>(row, base + p, a_chunk, K, a[p]);
         }
         // Nothing may be scheduled above this point: the first wait for an
         // operand would otherwise hold back the remaining loads.
@@ -148,9 +171,20 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
         for (int p = 0; p < PS; ++p) {
             // a step past the end (a re-read of the last one) must add nothing
             const bool live = base + p < S64;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) stage[mt * 64 + lane] = a[p][mt];
+            // LDS operations of one wavefront complete in order; the fences
+            // keep the compiler from moving the reads above the writes (or
+            // the next step's writes above these reads).
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             v4i ap[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) ap[mt] = live ? a[p][mt] : v4i{0, 0, 0, 0};
+            for (int mt = 0; mt < MT; ++mt) ap[mt] = live ? stage[mt * 64 + rd_slot] : v4i{0, 0, 0, 0};
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const v4i b = decode_b(bw[p][t]);
@@ -176,17 +210,12 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
             atomicAdd(&red[16 * mt + 4 * g + 3][16 * t + j], c[mt][t].w);
         }
     __syncthreads();
-    // Each thread writes four consecutive outputs of one row m: columns
-    // n0 .. n0 + 3 (fixed per thread, the stride being a multiple of 16),
-    // with 8-byte (bf16) and 16-byte (int32) stores where the row is aligned
-    // for them.
-    const int c4 = (tid & 15) * 4;
-    const int n0 = col * 64 + c4;
+    // Each thread writes four consecutive outputs of one row m, columns
+    // n0 .. n0 + 3, with 8-byte (bf16) and 16-byte (int32) stores where the
+    // row is aligned for them.
     float wsf[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        wsf[e] = bf16_to_float(
-            ws[(static_cast<uint64_t>(min(n0 + e, N - 1)) * seg_mul) >> seg_shift]);
+    for (int e = 0; e < 4; ++e) wsf[e] = bf16_to_float(wsb[e]);
     for (int i = tid; i < MT * 16 * 16; i += nthreads) {
         const int ml = i >> 4;
         const int m = m0 + ml;
