@@ -186,11 +186,11 @@ def layer_shapes(bl, steps, warmup):
     return out
 
 
-def batched(bl, steps, warmup):
+def batched(bl, steps, warmup, ms=synth.BATCHED_M):
     torch = _torch()
     out = {}
     lib = bl.lib()
-    for M in synth.BATCHED_M:
+    for M in ms:
         c = synth.batched(M)
         packed = bl.pack_ternary_weights(torch.from_numpy(c.w).cuda())
         n_copies = copies_for(packed.numel())
@@ -384,7 +384,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only")
-    ap.add_argument("--sections", default="fused,layer_set,batched,decode_step,ternarize,torch",
+    ap.add_argument("--sections", default="fused,layer_set,batched,prefill,decode_step,ternarize,torch",
                     help="detail sections to run after the headline (comma list; for profiling one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -428,6 +428,8 @@ def main():
         detail["layer_set_int8"] = layer_shapes(bl, max(args.steps // 4, 100), 50)
     if "batched" in sections:
         detail["batched_mfma"] = batched(bl, max(args.steps // 8, 50), 20)
+    if "prefill" in sections:
+        detail["prefill_13824x2560"] = batched(bl, 50, 10, synth.PREFILL_M)
     if "decode_step" in sections:
         detail["decode_step_graph"] = decode_step(bl, 20)
     if "ternarize" in sections:

@@ -49,6 +49,12 @@ hipError_t launch_gemv_bf16_fused(const uint16_t* x, const uint8_t* packed, cons
 hipError_t launch_ternarize(const uint16_t* w, uint8_t* packed, uint16_t* scales,
                             void* workspace, int N, int K, hipStream_t stream);
 
+// Many activation rows (prompt processing), int8 activations, int8 MFMA
+// with LDS-tiled reuse of both operands.
+hipError_t launch_gemm_prefill(const int8_t* xq, const uint8_t* packed, const float* s,
+                               const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int M,
+                               int N, int K, hipStream_t stream);
+
 // M >= 2, int8 activations, int8 MFMA.
 hipError_t launch_gemm_mfma(const int8_t* xq, const uint8_t* packed, const float* s,
                             const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int M,

@@ -37,6 +37,9 @@ LARGE_SET: List[Tuple[str, int, int, int]] = [
     ("large_5120x13824", 5120, 13824, 1),
 ]
 BATCHED_M = (16, 32, 64)
+# Prompt lengths of the pages' end-to-end latency table ([W2A8] §7.2): the
+# prompt-processing workload of the gate+up layer.
+PREFILL_M = (64, 256, 512)
 N_LAYERS = 30
 
 
@@ -169,7 +172,8 @@ def large_set() -> List[GemvF]:
 
 
 def batched(M: int) -> GemvF:
-    """M in {16, 32, 64}, (13824, 2560), ws_num=2: fp32 x ~ N(0, 1) to be quantised per row."""
+    """M rows (BATCHED_M, PREFILL_M), (13824, 2560), ws_num=2: fp32 x ~ N(0, 1) to be
+    quantised per row."""
     return make_float_gemv(f"batched_m{M}", M, 13824, 2560, 2, seed_for(4, 0, M))
 
 

@@ -42,6 +42,11 @@ def mfma_asm(tmp_path_factory):
     return _asm(tmp_path_factory, "gemm_mfma.hip")
 
 
+@pytest.fixture(scope="module")
+def prefill_asm(tmp_path_factory):
+    return _asm(tmp_path_factory, "gemm_prefill.hip")
+
+
 def test_weight_loads_issued_before_first_wait(gemv_asm):
     kernels = list(re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])ELi(\d)E\S*):", gemv_asm, re.M))
     assert len(kernels) == 120   # P = 1..20, int8 and bf16 input, C = 1, 2, 4 cached chunks
@@ -121,3 +126,23 @@ def test_no_scratch_and_declared_lds_only(gemv_asm, mfma_asm):
         # + the A staging slots, 8 wavefronts x MT x 1 KiB
         want = 16 * MT * (68 * 4 + 8 + 4) + 8 * MT * 1024
         assert _meta(mfma_asm, name, "amdhsa_group_segment_fixed_size") == want, name
+
+
+def test_prefill_no_scratch_and_declared_lds(prefill_asm):
+    # gemm_prefill_kernel<WN, WMW, MTW>: tile 64 WN weight rows x 16 MTW WMW
+    # activation rows; two LDS buffers of the activation tile (pitch 272)
+    # and the 4 WN weight tiles (1152 bytes each), nothing else.
+    kernels = list(re.finditer(r"^(_ZN\S*gemm_prefill_kernelILi(\d+)ELi(\d+)ELi(\d+)E\S*):",
+                               prefill_asm, re.M))
+    assert sorted((int(m.group(2)), int(m.group(3)), int(m.group(4))) for m in kernels) == \
+        [(1, 4, 1), (2, 4, 1), (4, 2, 2), (4, 2, 4)]
+    for m in kernels:
+        name = m.group(1)
+        WN, WMW, MTW = int(m.group(2)), int(m.group(3)), int(m.group(4))
+        BM, BN = 16 * MTW * WMW, 64 * WN
+        assert _meta(prefill_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
+        want = 2 * (BM * 272 + BN // 16 * 1152)
+        assert _meta(prefill_asm, name, "amdhsa_group_segment_fixed_size") == want, name
+        body = prefill_asm[m.end():prefill_asm.index("s_endpgm", m.end())]
+        # one K tile in the loop body: 4 steps x 4 bands x MTW m tiles
+        assert body.count("v_mfma_i32_16x16x64_i8") == 16 * MTW, name
