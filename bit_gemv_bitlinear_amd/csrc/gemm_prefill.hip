@@ -103,8 +103,19 @@ __global__ __launch_bounds__(WN * WMW * 64) void gemm_prefill_kernel(
     const int g = lane >> 4;
     const int nbands = (N + kTileRows - 1) / kTileRows;
     const int S256 = (K + kTileK - 1) / kTileK;
-    const int n_base = blockIdx.x * BN;
-    const int m_base = blockIdx.y * BM;
+    // Workgroups are dispatched to the eight XCDs in turn (id % 8).  The
+    // blocks of activation rows that share a block of weight rows get ids
+    // of one residue mod 8, so they run on one XCD and read those weight
+    // tiles through one L2; the grid is padded to a multiple of 8 weight
+    // blocks, and padding workgroups leave at once.
+    const int gx = (N + BN - 1) / BN;
+    const int gy = (M + BM - 1) / BM;
+    const int slot = static_cast<int>(blockIdx.x) >> 3;
+    const int nblk = static_cast<int>(blockIdx.x & 7) + 8 * (slot / gy);
+    const int mblk = slot % gy;
+    if (nblk >= gx) return;
+    const int n_base = nblk * BN;
+    const int m_base = mblk * BM;
 
     // Epilogue operands, loaded now so that nothing waits after the main
     // loop: the weight scales of this lane's 16 columns n (4 bands x 4
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(WN * WMW * 64) void gemm_prefill_kernel(
     for (int i = 0; i < kWTiles; ++i) {
         const int bb = wave + kWaves * i;
         w_has[i] = bb < kBands;   // uniform per wavefront
-        const int band = min(blockIdx.x * kBands + min(bb, kBands - 1), nbands - 1);
+        const int band = min(nblk * kBands + min(bb, kBands - 1), nbands - 1);
         w_src[i] = tiles + static_cast<size_t>(band) * S256 * 64 + lane;
         w_dst[i] = min(bb, kBands - 1) * kWTileWords + kWRowGroupWords * (lane >> 4) + 4 * (lane & 15);
     }
@@ -296,8 +307,9 @@ hipError_t launch_gemm_prefill(const int8_t* xq, const uint8_t* packed, const fl
             break;
         }
     }
-    const dim3 grid(static_cast<unsigned>((N + pick->bn - 1) / pick->bn),
-                    static_cast<unsigned>((M + pick->bm - 1) / pick->bm));
+    const int gx = (N + pick->bn - 1) / pick->bn;
+    const int gy = (M + pick->bm - 1) / pick->bm;
+    const dim3 grid(static_cast<unsigned>((gx + 7) / 8 * 8 * gy));
     uint32_t seg_mul;
     int seg_shift;
     seg_divisor(N / ws_num, seg_mul, seg_shift);
