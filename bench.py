@@ -335,7 +335,7 @@ def gemv_geometry(N, K):
     M=1 GEMV for this shape (the same rule as gemv_shape in bit_gemv_bitlinear_amd/csrc/gemv.hip)."""
     S = -(-K // 256)
     nbands = -(-N // 16)
-    target = 4 if nbands < 400 else 9
+    target = 4 if nbands < 400 else 10
     Wb = 1
     while Wb < 16 and -(-S // Wb) > target:
         Wb *= 2

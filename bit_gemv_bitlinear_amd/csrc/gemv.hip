@@ -428,8 +428,10 @@ constexpr int kMinGroups = 200;     // workgroups wanted in flight (256 CUs)
 // SIMDs with one wavefront, whose dot products after the last tile arrives
 // set the tail, so it takes shorter runs.  Measured same-box: at 2560 x 2560,
 // 3840 x 2560 and 2560 x 6912 the shorter runs gain 0.05-0.27 us; at
-// 13824 x 2560 they lose 0.5 us.
-constexpr int kTargetSteps = 9;
+// 13824 x 2560 they lose 0.5 us.  Wide matrices take runs of up to 10 (a
+// whole K = 2560 row per wavefront, half the wavefronts of runs of 5):
+// 0.05 us faster at 13824 x 2560.
+constexpr int kTargetSteps = 10;
 constexpr int kTargetStepsNarrow = 4;
 constexpr int kNarrowBands = 400;
 
