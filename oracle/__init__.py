@@ -55,7 +55,11 @@ def _load():
     lib.oracle_bitlinear_bf16.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
     lib.oracle_absmean_scales.argtypes = [ctypes.c_uint16, P, P]
     lib.oracle_ternary_from_scale.argtypes = [P, ctypes.c_size_t, ctypes.c_uint16, P]
-    for name in ("oracle_absmean_scales", "oracle_ternary_from_scale", "oracle_quant_absmax_i8_f32", "oracle_quant_absmax_i8_bf16", "oracle_unpack_tiles",
+    lib.oracle_rmsnorm_bf16.argtypes = [P, P, I, ctypes.c_float, P]
+    lib.oracle_relu2_glu_bf16.argtypes = [P, P, I, P]
+    lib.oracle_add_bf16.argtypes = [P, P, I, P]
+    for name in ("oracle_rmsnorm_bf16", "oracle_relu2_glu_bf16", "oracle_add_bf16",
+                 "oracle_absmean_scales", "oracle_ternary_from_scale", "oracle_quant_absmax_i8_f32", "oracle_quant_absmax_i8_bf16", "oracle_unpack_tiles",
                  "oracle_gemm_i32", "oracle_epilogue_bf16", "oracle_bitlinear_i8",
                  "oracle_bitlinear_bf16"):
         getattr(lib, name).restype = ctypes.c_int
@@ -295,3 +299,57 @@ def ternarize_absmean(w_bits):
     q = np.empty(w.shape, dtype=np.int8)
     _check(lib.oracle_ternary_from_scale(_ptr(w), w.size, s_b.value, _ptr(q)), "ternary_from_scale")
     return q, mean, int(s_b.value), int(ws_b.value)
+
+
+# --------------------------------------------------------------------------
+# Glue between a block's projections  ([W2A8] §4.1 names the norms and the
+# fused projections; the formulas are readings stated in oracle.c)
+# --------------------------------------------------------------------------
+
+RMS_EPS = np.float32(1e-5)
+
+
+def rmsnorm_bf16(x_bits, g_bits, eps=RMS_EPS):
+    """RMSNorm of a bf16 row with a bf16 weight, fp64, rounded once to bf16 (bits)."""
+    x = _c(x_bits, np.uint16).reshape(-1)
+    g = _c(g_bits, np.uint16).reshape(-1)
+    if x.size != g.size:
+        raise OracleError("rmsnorm sizes")
+    y = np.empty_like(x)
+    _check(_load().oracle_rmsnorm_bf16(_ptr(x), _ptr(g), x.size, float(eps), _ptr(y)), "rmsnorm_bf16")
+    return y
+
+
+def relu2_glu_bf16(gate_bits, up_bits):
+    """bf16(max(gate, 0)^2 * up), elementwise (bits)."""
+    a = _c(gate_bits, np.uint16).reshape(-1)
+    b = _c(up_bits, np.uint16).reshape(-1)
+    if a.size != b.size:
+        raise OracleError("glu sizes")
+    m = np.empty_like(a)
+    _check(_load().oracle_relu2_glu_bf16(_ptr(a), _ptr(b), a.size, _ptr(m)), "relu2_glu_bf16")
+    return m
+
+
+def add_bf16(a_bits, b_bits):
+    """bf16(a + b), elementwise (bits)."""
+    a = _c(a_bits, np.uint16).reshape(-1)
+    b = _c(b_bits, np.uint16).reshape(-1)
+    if a.size != b.size:
+        raise OracleError("add sizes")
+    out = np.empty_like(a)
+    _check(_load().oracle_add_bf16(_ptr(a), _ptr(b), a.size, _ptr(out)), "add_bf16")
+    return out
+
+
+def norm_bitlinear(x_bits, g_bits, w, ws_bits, ws_num, up_bits=None, residual_bits=None,
+                   eps=RMS_EPS):
+    """One projection of a block at M = 1: [relu2-GLU of (x, up)] -> RMSNorm(g) -> per-token
+    int8 quantisation -> ternary layer -> [+ residual].  Returns (xn, q, s, acc, y)."""
+    m = x_bits if up_bits is None else relu2_glu_bf16(x_bits, up_bits)
+    xn = rmsnorm_bf16(m, g_bits, eps)
+    q, s, acc, y = bitlinear_bf16(xn.reshape(1, -1), w, ws_bits, ws_num)
+    y = y.reshape(-1)
+    if residual_bits is not None:
+        y = add_bf16(residual_bits, y)
+    return xn, q.reshape(-1), s, acc.reshape(-1), y

@@ -28,6 +28,10 @@
  *   absmean_scales,  ternarise a bf16 weight matrix by its mean absolute
  *   ternary_from_scale  value: s = 1/mean, Wt = clamp(round(W*s), -1, 1),
  *                    ws = 1/s, in the page's bf16 arithmetic       [W2A8] §4.2
+ *   rmsnorm_bf16,    the glue between a block's projections: the norms,
+ *   relu2_glu_bf16,  the MLP activation and the residual adds of the model
+ *   add_bf16         the page converts (names only; formulas are readings,
+ *                    stated at the functions)                      [W2A8] §4.1
  *
  * Readings where the page is ambiguous (each one is listed with its reason in
  * the design notes):
@@ -402,5 +406,69 @@ int oracle_ternary_from_scale(const uint16_t* w, size_t n, uint16_t s_bits, int8
             r = -1.0f;
         q[i] = (int8_t)r;
     }
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Glue between the layers of a block (decode step chained through the     */
+/* model's norms, activation and residuals)                                 */
+/* ---------------------------------------------------------------------- */
+/*
+ * [W2A8] §4.1 names the norms of the model it converts -- attention_norm and
+ * ffn_norm before the attention and MLP inputs, and BitNet b1.58's own
+ * attn_sub_norm and ffn_sub_norm -- and the fused projections wqkv, wo, w13
+ * (gate_proj then up_proj) and w2, but states neither the norm's formula
+ * nor the MLP activation.  Readings (each listed with its reason in the
+ * design notes): every norm is an RMSNorm with a bf16 weight and
+ * eps = fp32(1e-5); the MLP activation is the squared ReLU of the gate half
+ * times the up half of w13's output; a residual adds two bf16 vectors.  All
+ * of it runs in fp64 and is rounded once to bf16.
+ */
+
+/* y[i] = bf16( fl64(x[i] * g[i]) * fl64(1 / sqrt(sum_j x[j]^2 / K + eps)) ):
+ * the inverse root mean square of the row (the sum taken in fp64 in index
+ * order), applied to the exact product of the element and its weight. */
+int oracle_rmsnorm_bf16(const uint16_t* x, const uint16_t* g, int K, float eps, uint16_t* y)
+{
+    if (!x || !g || !y || K < 1 || !(eps >= 0.0f))
+        return OR_ERR_ARG;
+    double sum = 0.0;
+    for (int i = 0; i < K; ++i) {
+        double v = (double)bf16_bits_to_float(x[i]);
+        sum += v * v;
+    }
+    double inv = 1.0 / sqrt(sum / (double)K + (double)eps);
+    for (int i = 0; i < K; ++i) {
+        double prod = (double)bf16_bits_to_float(x[i]) * (double)bf16_bits_to_float(g[i]);
+        y[i] = oracle_bf16_rne(prod * inv);
+    }
+    return OR_OK;
+}
+
+/* m[i] = bf16( max(gate[i], 0)^2 * up[i] ), exact in fp64 before the
+ * rounding (a bf16 has 8 significant bits, so the product has at most 24,
+ * and its exponent stays inside fp64's range). */
+int oracle_relu2_glu_bf16(const uint16_t* gate, const uint16_t* up, int K, uint16_t* m)
+{
+    if (!gate || !up || !m || K < 1)
+        return OR_ERR_ARG;
+    for (int i = 0; i < K; ++i) {
+        double a = (double)bf16_bits_to_float(gate[i]);
+        double r = a > 0.0 ? a : 0.0;
+        m[i] = oracle_bf16_rne(r * r * (double)bf16_bits_to_float(up[i]));
+    }
+    return OR_OK;
+}
+
+/* out[i] = bf16( a[i] + b[i] ): the fp64 sum of two bf16 values is exact
+ * unless their exponents differ by more than 45, and then the smaller lies
+ * far below half a bf16 unit of the larger, so rounding that sum gives the
+ * bf16 of the exact sum either way. */
+int oracle_add_bf16(const uint16_t* a, const uint16_t* b, int n, uint16_t* out)
+{
+    if (!a || !b || !out || n < 0)
+        return OR_ERR_ARG;
+    for (int i = 0; i < n; ++i)
+        out[i] = oracle_bf16_rne((double)bf16_bits_to_float(a[i]) + (double)bf16_bits_to_float(b[i]));
     return OR_OK;
 }

@@ -1,0 +1,188 @@
+"""Pins of the oracle's glue between a block's projections: RMSNorm, the
+squared-ReLU GLU and the residual add (readings of the model [W2A8] §4.1
+names; see oracle.c).
+
+Each is checked against something other than the oracle itself: exact
+rational arithmetic (Python Fractions, with bf16 round-to-nearest-even
+written out from the format's definition here), torch's fp64 rms_norm as a
+library reference, and closed forms / invariants.
+"""
+import math
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+EPS = Fraction(float(np.float32(1e-5)))
+
+
+def bits_to_fraction(b):
+    f = struct.unpack("<f", struct.pack("<I", int(b) << 16))[0]
+    return Fraction(f)
+
+
+def bf16_bits_of_exact(v: Fraction) -> int:
+    """Round a rational to bf16 (nearest, ties to even) from the format's definition."""
+    if v == 0:
+        return 0
+    sign = 0x8000 if v < 0 else 0
+    a = -v if v < 0 else v
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    spacing = Fraction(2) ** (max(e, -126) - 7)
+    q = a / spacing
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    r = n * spacing
+    if r >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    u = struct.unpack("<I", struct.pack("<f", float(r)))[0]
+    assert u & 0xFFFF == 0
+    return sign | (u >> 16)
+
+
+def rmsnorm_exact(x_bits, g_bits, eps=EPS):
+    """bf16 of x*g / sqrt(sum(x^2)/K + eps), decided exactly (squares compared as rationals)."""
+    xs = [bits_to_fraction(b) for b in x_bits]
+    gs = [bits_to_fraction(b) for b in g_bits]
+    D = sum(v * v for v in xs) / len(xs) + eps
+    out = []
+    for xv, gv, xb, gb in zip(xs, gs, x_bits, g_bits):
+        num = xv * gv
+        if num == 0:
+            # IEEE product of zeros: sign is the exclusive or of the signs
+            out.append(0x8000 if ((int(xb) ^ int(gb)) & 0x8000) else 0)
+            continue
+        sign = 0x8000 if num < 0 else 0
+        a = abs(num)
+        approx = float(a) / math.sqrt(float(D))
+        c = bf16_bits_of_exact(Fraction(approx)) & 0x7FFF
+        # the exact value a/sqrt(D) against the midpoints around candidates c-1, c, c+1
+        best = None
+        for cand in (c - 1, c, c + 1):
+            if cand < 0 or cand >= 0x7F80:
+                continue
+            lo = bits_to_fraction(cand - 1) if cand > 0 else Fraction(0)
+            hi = bits_to_fraction(cand + 1)
+            cv = bits_to_fraction(cand)
+            m_lo = (lo + cv) / 2
+            m_hi = (cv + hi) / 2
+            # m_lo <= a/sqrt(D) <= m_hi  <=>  m_lo^2 D <= a^2 <= m_hi^2 D (all positive)
+            a2 = a * a
+            below = a2 < m_lo * m_lo * D
+            above = a2 > m_hi * m_hi * D
+            if below or above:
+                continue
+            if a2 == m_lo * m_lo * D and cand % 2 == 1:
+                continue
+            if a2 == m_hi * m_hi * D and cand % 2 == 1:
+                continue
+            best = cand
+            break
+        assert best is not None
+        out.append(sign | best)
+    return np.array(out, dtype=np.uint16)
+
+
+def rand_bf16(g, n, scale=1.0):
+    return oracle.bf16_rne(g.normal(size=n) * scale)
+
+
+@pytest.mark.parametrize("K,scale", [(1, 1.0), (7, 3.0), (64, 1.0), (300, 0.01), (2560, 1.0)])
+def test_rmsnorm_against_exact(K, scale):
+    g = np.random.default_rng(100 + K)
+    x = rand_bf16(g, K, scale)
+    w = oracle.bf16_rne(1.0 + 0.1 * g.normal(size=K))
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(x, w), rmsnorm_exact(x, w))
+
+
+def test_rmsnorm_wide_range_against_exact():
+    g = np.random.default_rng(7)
+    x = oracle.bf16_rne(g.normal(size=200) * np.exp2(g.integers(-40, 20, size=200)))
+    x[:3] = [0, 0x8000, 0x3F80]      # +0, -0, 1.0
+    w = oracle.bf16_rne(g.normal(size=200))
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(x, w), rmsnorm_exact(x, w))
+
+
+def test_rmsnorm_against_torch_fp64():
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(11)
+    K = 6912
+    x = rand_bf16(g, K)
+    w = oracle.bf16_rne(1.0 + 0.2 * g.normal(size=K))
+    xt = torch.from_numpy(oracle.bf16_to_f32(x).astype(np.float64))
+    wt = torch.from_numpy(oracle.bf16_to_f32(w).astype(np.float64))
+    ref = torch.nn.functional.rms_norm(xt, (K,), weight=wt, eps=float(np.float32(1e-5)))
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(x, w), oracle.bf16_rne(ref.numpy()))
+
+
+def test_rmsnorm_closed_forms():
+    one = np.full(16, 0x3F80, dtype=np.uint16)
+    # constant row c with weight 1: c / sqrt(c^2 + eps) = 0.999995 -> 1.0 for c = 1
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(one, one), one)
+    # zero row -> zeros; zero weight -> zeros
+    zero = np.zeros(16, dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(zero, one), zero)
+    g = np.random.default_rng(3)
+    x = rand_bf16(g, 16)
+    assert not np.any(oracle.rmsnorm_bf16(x, zero) & 0x7FFF)
+    # without eps the norm is invariant under scaling by a power of two
+    w = oracle.bf16_rne(g.normal(size=16))
+    x2 = oracle.bf16_rne(oracle.bf16_to_f32(x).astype(np.float64) * 2.0 ** 9)
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(x, w, eps=0.0), oracle.rmsnorm_bf16(x2, w, eps=0.0))
+    # a single element: x / sqrt(x^2 + eps) -> sign(x) * w for |x| >> sqrt(eps)
+    np.testing.assert_array_equal(
+        oracle.rmsnorm_bf16(np.array([0xC080], np.uint16), np.array([0x4000], np.uint16)),
+        np.array([0xC000], np.uint16))
+
+
+def exact_glu(gb, ub):
+    gv, uv = bits_to_fraction(gb), bits_to_fraction(ub)
+    r = gv if gv > 0 else Fraction(0)
+    v = r * r * uv
+    if v == 0:
+        # fp64: (+0) * up keeps up's sign
+        return 0x8000 if (int(ub) & 0x8000) else 0
+    return bf16_bits_of_exact(v)
+
+
+def test_relu2_glu_against_exact():
+    g = np.random.default_rng(5)
+    gate = rand_bf16(g, 500, 2.0)
+    up = rand_bf16(g, 500, 2.0)
+    gate[:4] = [0, 0x8000, 0x3F80, 0xBF80]   # +0, -0, 1, -1
+    up[:4] = [0xBF80, 0x3F80, 0xC040, 0x4040]
+    want = np.array([exact_glu(a, b) for a, b in zip(gate, up)], dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.relu2_glu_bf16(gate, up), want)
+
+
+def test_relu2_glu_closed_forms():
+    # negative gate -> signed zero; gate 2, up 3 -> 12; overflow -> inf
+    gate = np.array([0xC000, 0x4000, 0x7100], dtype=np.uint16)     # -2, 2, 2^99
+    up = np.array([0x4040, 0x4040, 0x7100], dtype=np.uint16)       # 3, 3, 2^99
+    np.testing.assert_array_equal(oracle.relu2_glu_bf16(gate, up),
+                                  np.array([0x0000, 0x4140, 0x7F80], dtype=np.uint16))
+
+
+def test_add_against_exact():
+    g = np.random.default_rng(9)
+    a = rand_bf16(g, 1000)
+    b = oracle.bf16_rne(g.normal(size=1000) * np.exp2(g.integers(-60, 8, size=1000)))
+    b[:3] = [a[0] ^ 0x8000, 0, 0x8000]       # cancellation -> +0, and signed zeros
+    want = []
+    for x, y in zip(a, b):
+        v = bits_to_fraction(x) + bits_to_fraction(y)
+        if v == 0:
+            both_neg = (int(x) & 0x8000) and (int(y) & 0x8000)
+            want.append(0x8000 if both_neg else 0)
+        else:
+            want.append(bf16_bits_of_exact(v))
+    np.testing.assert_array_equal(oracle.add_bf16(a, b), np.array(want, dtype=np.uint16))
