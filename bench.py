@@ -268,6 +268,57 @@ def decode_step(bl, reps):
             "bytes_per_step": nbytes, "gemvs_per_step": len(calls)}
 
 
+def chained_step(bl, reps):
+    """The decode step chained through its glue (readings of the norms and MLP activation the
+    pages name): 30 layers x {qkv after attention_norm, o after attn_sub_norm + residual,
+    gate+up after ffn_norm, down after relu(gate)^2 * up and ffn_sub_norm + residual}; one
+    kernel per projection, one bl_graph per step.  The attention is out of scope: each layer's
+    o reads a seeded attention output."""
+    torch = _torch()
+    dim, ffn = synth.DIM, synth.FFN
+    h = [bf16_dev(synth.chained_h0())] + [torch.empty(dim, dtype=torch.bfloat16, device="cuda")
+                                          for _ in range(synth.N_LAYERS)]
+    calls, nbytes = [], 0
+    for l in range(synth.N_LAYERS):
+        L = synth.chained_layer(l)
+        p = {k: bl.pack_ternary_weights(torch.from_numpy(v).cuda()) for k, v in L.w.items()}
+        wsd = {k: bf16_dev(v) for k, v in L.ws.items()}
+        gm = {k: bf16_dev(v) for k, v in L.gamma.items()}
+        qkv = torch.empty(3840, dtype=torch.bfloat16, device="cuda")
+        h1 = torch.empty(dim, dtype=torch.bfloat16, device="cuda")
+        gu = torch.empty(2 * ffn, dtype=torch.bfloat16, device="cuda")
+        calls += [
+            dict(x=h[l], gamma=gm["attn"], packed=p["qkv"], ws=wsd["qkv"], ws_num=1, y=qkv,
+                 N=3840, K=dim),
+            dict(x=bf16_dev(L.attn_out), gamma=gm["attn_sub"], packed=p["o"], ws=wsd["o"], ws_num=1,
+                 residual=h[l], y=h1, N=dim, K=dim),
+            dict(x=h1, gamma=gm["ffn"], packed=p["gate_up"], ws=wsd["gate_up"], ws_num=2, y=gu,
+                 N=2 * ffn, K=dim),
+            dict(x=gu[:ffn], x_up=gu[ffn:], gamma=gm["ffn_sub"], packed=p["down"], ws=wsd["down"],
+                 ws_num=1, residual=h1, y=h[l + 1], N=dim, K=ffn),
+        ]
+    for c in calls:
+        # weights + scales + bf16 row (twice for the GLU) + its weight + output (+ residual)
+        nbytes += gemv_bytes(1, c["N"], c["K"], c["ws_num"], x_bytes=2)
+        nbytes += 2 * c["K"] * (2 if c.get("x_up") is not None else 1) - 2 * c["K"]
+        nbytes += 2 * c["K"] + (2 * c["N"] if c.get("residual") is not None else 0)
+    g = bl.ChainedDecodeGraph(calls)
+    for _ in range(3):
+        g.launch()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.launch()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    g.close()
+    return {"us_per_step": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "bytes_per_step": nbytes, "projections_per_step": len(calls)}
+
+
 def torch_bf16_context(steps):
     """The page's comparison column: torch bf16 matmul, 1 x 2560 by 2560 x 13824, weights rotated."""
     torch = _torch()
@@ -384,7 +435,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only")
-    ap.add_argument("--sections", default="fused,layer_set,batched,prefill,decode_step,ternarize,torch",
+    ap.add_argument("--sections",
+                    default="fused,layer_set,batched,prefill,decode_step,chained_step,ternarize,torch",
                     help="detail sections to run after the headline (comma list; for profiling one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -432,6 +484,8 @@ def main():
         detail["prefill_13824x2560"] = batched(bl, 50, 10, synth.PREFILL_M)
     if "decode_step" in sections:
         detail["decode_step_graph"] = decode_step(bl, 20)
+    if "chained_step" in sections:
+        detail["chained_decode_step_graph"] = chained_step(bl, 20)
     if "ternarize" in sections:
         detail["ternarize_pack_bf16_13824x2560"] = ternarize(bl, 50, 10)
     if "torch" in sections:

@@ -21,6 +21,9 @@ TERNARIZE_WORKSPACE_BYTES = 2048   # BL_TERNARIZE_WORKSPACE_BYTES
 # Largest K the single-kernel M = 1 paths take (include/bitlinear.h); beyond it the
 # bf16 entry needs staging buffers for the quantised activations.
 GEMV_MAX_K = 61440
+# Largest K of the projection with its glue (bitlinear_rmsnorm_i8xi2).
+NORM_MAX_K = 32768
+RMS_EPS = 1e-5
 
 # Entry points declared in include/bitlinear.h: name -> (restype, argtypes).
 _P = ctypes.c_void_p
@@ -35,7 +38,10 @@ SIGNATURES = {
     "quantize_act_absmax_i8": (_I, [_P, _I, _P, _P, _I, _I, _P]),
     "bitlinear_i8xi2": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _P]),
     "bitlinear_bf16_i8xi2": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "bitlinear_rmsnorm_i8xi2": (_I, [_P, _P, _P, ctypes.c_float, _P, _P, _I, _P, _P, _P, _P, _P,
+                                     _P, _I, _I, _P]),
     "bl_graph_create": (_I, [_P, _I, ctypes.POINTER(_P)]),
+    "bl_graph_create_norm": (_I, [_P, _I, ctypes.POINTER(_P)]),
     "bl_graph_launch": (_I, [_P, _P]),
     "bl_graph_size": (_I, [_P]),
     "bl_graph_destroy": (_I, [_P]),
@@ -51,6 +57,11 @@ class BitLinearError(RuntimeError):
 class bl_gemv_desc(ctypes.Structure):
     _fields_ = [("x", _P), ("packed", _P), ("ws", _P), ("ws_num", _I), ("y", _P), ("acc", _P),
                 ("N", _I), ("K", _I)]
+
+
+class bl_norm_desc(ctypes.Structure):
+    _fields_ = [("x", _P), ("x_up", _P), ("gamma", _P), ("eps", ctypes.c_float), ("packed", _P),
+                ("ws", _P), ("ws_num", _I), ("residual", _P), ("y", _P), ("N", _I), ("K", _I)]
 
 
 _lib = None
@@ -219,6 +230,31 @@ def bitlinear_bf16_i8xi2(x, packed, ws, N, ws_num=None, y=None, q_out=None, s_ou
     return y
 
 
+def bitlinear_rmsnorm_i8xi2(x, packed, gamma, ws, N, ws_num=None, x_up=None, residual=None,
+                            eps=RMS_EPS, y=None, xn_out=None, q_out=None, s_out=None, acc=None):
+    """One projection with its glue (M = 1): [relu(x)^2 * x_up] -> RMSNorm(gamma, eps) ->
+    per-token int8 quantisation -> the layer -> [+ residual].  Returns y (bf16, N)."""
+    import torch
+    _require(x, torch.bfloat16, "x")
+    _require(gamma, torch.bfloat16, "gamma")
+    _require(packed, torch.uint8, "packed")
+    _require(ws, torch.bfloat16, "ws")
+    K = x.numel()
+    ws_num = ws.numel() if ws_num is None else ws_num
+    if packed.numel() != bl_packed_bytes(N, K):
+        raise ValueError("packed has the wrong size for (N, K)")
+    if gamma.numel() != K or (x_up is not None and x_up.numel() != K):
+        raise ValueError("gamma and x_up must have K elements")
+    if y is None:
+        y = torch.empty((N,), dtype=torch.bfloat16, device=x.device)
+    _check(lib().bitlinear_rmsnorm_i8xi2(_ptr(x), _ptr(x_up), _ptr(gamma), float(eps),
+                                         _ptr(packed), _ptr(ws), ws_num, _ptr(residual),
+                                         _ptr(y), _ptr(xn_out), _ptr(q_out), _ptr(s_out),
+                                         _ptr(acc), N, K, _stream()),
+           "bitlinear_rmsnorm_i8xi2")
+    return y
+
+
 class DecodeGraph:
     """A chain of M = 1 bf16 layer calls captured once (bl_graph_create) and replayed.
 
@@ -254,3 +290,23 @@ class DecodeGraph:
             self.close()
         except Exception:
             pass
+
+
+class ChainedDecodeGraph(DecodeGraph):
+    """A decode step chained through its glue (bl_graph_create_norm): ``calls`` is a list of
+    dicts with keys x, gamma, packed, ws, ws_num, y, N, K and optionally x_up, residual, eps;
+    each call may read an earlier call's y.  The tensors must stay alive with the graph."""
+
+    def __init__(self, calls):
+        self._keep = calls
+        arr = (bl_norm_desc * len(calls))()
+
+        def p(c, k):
+            return c[k].data_ptr() if c.get(k) is not None else None
+        for i, c in enumerate(calls):
+            arr[i] = bl_norm_desc(p(c, "x"), p(c, "x_up"), p(c, "gamma"), float(c.get("eps", RMS_EPS)),
+                                  p(c, "packed"), p(c, "ws"), c["ws_num"], p(c, "residual"),
+                                  p(c, "y"), c["N"], c["K"])
+        h = ctypes.c_void_p()
+        _check(lib().bl_graph_create_norm(arr, len(calls), ctypes.byref(h)), "bl_graph_create_norm")
+        self._h = h

@@ -72,6 +72,24 @@ int check_layer_bf16(const uint16_t* x, const uint8_t* packed, const uint16_t* w
 constexpr int kPrefillMinM = 128;
 constexpr int kPrefillMinN = 8192;
 
+int check_norm(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma, float eps,
+               const uint8_t* packed, const uint16_t* ws, int ws_num, const uint16_t* residual,
+               const uint16_t* y, const uint16_t* xn_out, const int8_t* q_out,
+               const float* s_out, const int32_t* acc, int N, int K) {
+    if (!x || !gamma || !packed || !ws || !y) return BL_ERR_NULL;
+    int rc = check_mnk(1, N, K);
+    if (rc) return rc;
+    if (K > bl::kNormMaxK) return BL_ERR_SHAPE;
+    if ((rc = check_ws(ws_num, N))) return rc;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return BL_ERR_ARG;
+    if (!aligned(x, 16) || (x_up && !aligned(x_up, 16)) || !aligned(gamma, 16) ||
+        !aligned(packed, 16) || !aligned(ws, 2) || (residual && !aligned(residual, 2)) ||
+        !aligned(y, 2) || (xn_out && !aligned(xn_out, 16)) || (q_out && !aligned(q_out, 8)) ||
+        (s_out && !aligned(s_out, 4)) || (acc && !aligned(acc, 4)))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
 int run_layer_i8(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,
                  int ws_num, uint16_t* y, int32_t* acc, int M, int N, int K, hipStream_t stream) {
     if (M == 1 && K <= bl::kGemvMaxK)
@@ -98,6 +116,44 @@ struct bl_graph {
     hipGraphExec_t exec;
     int n;
 };
+
+namespace {
+
+// Capture n calls (enqueue(i, stream) -> status) on an internal stream and
+// instantiate them into a bl_graph.
+template <class Enqueue>
+int capture_graph(int n, bl_graph** out, Enqueue enqueue) {
+    (void)hipGetLastError();
+    hipStream_t cs = nullptr;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return BL_ERR_HIP;
+    int rc = BL_OK;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        rc = BL_ERR_HIP;
+    } else {
+        for (int i = 0; i < n && rc == BL_OK; ++i) rc = enqueue(i, cs);
+        const hipError_t e = hipStreamEndCapture(cs, &graph);
+        if (rc == BL_OK && e != hipSuccess) rc = BL_ERR_HIP;
+    }
+    if (rc == BL_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess)
+        rc = BL_ERR_HIP;
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(cs);
+    if (rc != BL_OK) {
+        if (exec) (void)hipGraphExecDestroy(exec);
+        return rc;
+    }
+    bl_graph* g = new (std::nothrow) bl_graph{exec, n};
+    if (!g) {
+        (void)hipGraphExecDestroy(exec);
+        return BL_ERR_ARG;
+    }
+    *out = g;
+    return BL_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -172,6 +228,19 @@ int bitlinear_bf16_i8xi2(const uint16_t* x, const uint8_t* packed, const uint16_
     return run_layer_bf16(x, packed, ws, ws_num, y, q_out, s_out, acc, M, N, K, stream);
 }
 
+int bitlinear_rmsnorm_i8xi2(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma,
+                            float eps, const uint8_t* packed, const uint16_t* ws, int ws_num,
+                            const uint16_t* residual, uint16_t* y, uint16_t* xn_out,
+                            int8_t* q_out, float* s_out, int32_t* acc, int N, int K,
+                            hipStream_t stream) {
+    const int rc = check_norm(x, x_up, gamma, eps, packed, ws, ws_num, residual, y, xn_out, q_out,
+                              s_out, acc, N, K);
+    if (rc) return rc;
+    (void)hipGetLastError();
+    return status_of(bl::launch_gemv_norm(x, x_up, gamma, eps, packed, ws, ws_num, residual, y,
+                                          xn_out, q_out, s_out, acc, N, K, stream));
+}
+
 int bl_graph_create(const bl_gemv_desc* descs, int n, bl_graph** out) {
     if (!out) return BL_ERR_NULL;
     *out = nullptr;
@@ -183,38 +252,30 @@ int bl_graph_create(const bl_gemv_desc* descs, int n, bl_graph** out) {
                                         d.acc, 1, d.N, d.K);
         if (rc) return rc;
     }
-    (void)hipGetLastError();
-    hipStream_t cs = nullptr;
-    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return BL_ERR_HIP;
-    int rc = BL_OK;
-    hipGraph_t graph = nullptr;
-    hipGraphExec_t exec = nullptr;
-    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
-        rc = BL_ERR_HIP;
-    } else {
-        for (int i = 0; i < n && rc == BL_OK; ++i) {
-            const bl_gemv_desc& d = descs[i];
-            rc = run_layer_bf16(d.x, d.packed, d.ws, d.ws_num, d.y, nullptr, nullptr, d.acc, 1,
-                                d.N, d.K, cs);
-        }
-        const hipError_t e = hipStreamEndCapture(cs, &graph);
-        if (rc == BL_OK && e != hipSuccess) rc = BL_ERR_HIP;
+    return capture_graph(n, out, [&](int i, hipStream_t cs) {
+        const bl_gemv_desc& d = descs[i];
+        return run_layer_bf16(d.x, d.packed, d.ws, d.ws_num, d.y, nullptr, nullptr, d.acc, 1, d.N,
+                              d.K, cs);
+    });
+}
+
+int bl_graph_create_norm(const bl_norm_desc* descs, int n, bl_graph** out) {
+    if (!out) return BL_ERR_NULL;
+    *out = nullptr;
+    if (!descs) return BL_ERR_NULL;
+    if (n < 1 || n > 65536) return BL_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        const bl_norm_desc& d = descs[i];
+        const int rc = check_norm(d.x, d.x_up, d.gamma, d.eps, d.packed, d.ws, d.ws_num,
+                                  d.residual, d.y, nullptr, nullptr, nullptr, nullptr, d.N, d.K);
+        if (rc) return rc;
     }
-    if (rc == BL_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess)
-        rc = BL_ERR_HIP;
-    if (graph) (void)hipGraphDestroy(graph);
-    (void)hipStreamDestroy(cs);
-    if (rc != BL_OK) {
-        if (exec) (void)hipGraphExecDestroy(exec);
-        return rc;
-    }
-    bl_graph* g = new (std::nothrow) bl_graph{exec, n};
-    if (!g) {
-        (void)hipGraphExecDestroy(exec);
-        return BL_ERR_ARG;
-    }
-    *out = g;
-    return BL_OK;
+    return capture_graph(n, out, [&](int i, hipStream_t cs) {
+        const bl_norm_desc& d = descs[i];
+        return status_of(bl::launch_gemv_norm(d.x, d.x_up, d.gamma, d.eps, d.packed, d.ws,
+                                              d.ws_num, d.residual, d.y, nullptr, nullptr,
+                                              nullptr, nullptr, d.N, d.K, cs));
+    });
 }
 
 int bl_graph_launch(bl_graph* graph, hipStream_t stream) {

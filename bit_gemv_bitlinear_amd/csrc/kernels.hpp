@@ -32,6 +32,7 @@ struct GemvShape {
     int bands;
 };
 constexpr int kGemvMaxK = 61440;   // LDS copy of the row <= 60 KiB
+constexpr int kNormMaxK = 32768;   // the projection with its glue (launch_gemv_norm)
 GemvShape gemv_shape(int N, int K);
 
 // M == 1, int8 activations; K <= kGemvMaxK.
@@ -43,6 +44,15 @@ hipError_t launch_gemv_i8(const int8_t* xq, const uint8_t* packed, const float* 
 hipError_t launch_gemv_bf16_fused(const uint16_t* x, const uint8_t* packed, const uint16_t* ws,
                                   int ws_num, uint16_t* y, int8_t* q_out, float* s_out,
                                   int32_t* acc, int N, int K, hipStream_t stream);
+
+// M == 1 projection with its glue: [relu2-GLU of (x, x_up)] -> RMSNorm(gamma,
+// eps) -> per-token int8 quantisation -> ternary layer -> [+ residual];
+// K <= kNormMaxK.  xn_out / q_out / s_out / acc may be null.
+hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma,
+                            float eps, const uint8_t* packed, const uint16_t* ws, int ws_num,
+                            const uint16_t* residual, uint16_t* y, uint16_t* xn_out,
+                            int8_t* q_out, float* s_out, int32_t* acc, int N, int K,
+                            hipStream_t stream);
 
 // Ternarise a bf16 N x K matrix by its mean |w| and pack it; scales[0..2] =
 // ws, s, mean (bf16); workspace: 256 uint64 (the exponent histogram).

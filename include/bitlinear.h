@@ -204,6 +204,45 @@ int bitlinear_bf16_i8xi2(const uint16_t* x, const uint8_t* packed, const uint16_
                          int M, int N, int K, hipStream_t stream);
 
 /*
+ * bitlinear_rmsnorm_i8xi2 -- one projection of a decode step with the glue
+ * that joins it to the previous one.  [W2A8] §4.1 names the converted
+ * model's norms (attention_norm and ffn_norm before the attention and MLP
+ * inputs, BitNet b1.58's attn_sub_norm and ffn_sub_norm) and its fused
+ * projections (wqkv, wo, w13 = gate_proj then up_proj, w2) but states
+ * neither the norm's formula nor the MLP activation; this library reads
+ * them as RMSNorm and relu(gate)^2 * up:
+ *   m    = x                              (x_up == NULL)
+ *        = bf16(max(x, 0)^2 * x_up)       (x_up != NULL: x and x_up are the
+ *                                          gate and up halves of w13's output)
+ *   xn   = bf16( fl64(m * gamma) * fl64(1 / sqrt(sum(m^2) / K + eps)) )
+ *   q, s = per-token absmax int8 quantisation of xn, as quantize_act_absmax_i8
+ *   y    = bf16(acc * ws / s), or bf16(residual + bf16(acc * ws / s))
+ *   x, x_up, gamma  device, bf16, K, 16-byte aligned (x_up may be NULL)
+ *   eps       finite, >= 0 (the model's: 1e-5)
+ *   packed, ws, ws_num   as bitlinear_i8xi2
+ *   residual  device, bf16, N, or NULL
+ *   y         device, bf16, N
+ *   xn_out    device, bf16, K, 16-byte aligned, or NULL: the normalised row
+ *   q_out     device, int8, K, 8-byte aligned, or NULL
+ *   s_out     device, fp32, 1, or NULL
+ *   acc       device, int32, N, or NULL
+ * One row (M = 1), 16 <= K <= 32768 with K % 16 == 0.  One kernel: every
+ * workgroup forms the glue for its copy of the row, then runs the GEMV.
+ * y must not overlap x, x_up or gamma (other workgroups still read them);
+ * it may be residual itself (each output reads only its own residual).
+ * xn matches the fp64 definition except, possibly, when that value lies
+ * within about 2^-50 (relative) of a bf16 rounding midpoint (the sum of
+ * squares is taken in another order), where it may be the other neighbour.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_ARG (eps or
+ * ws_num), BL_ERR_HIP.
+ */
+int bitlinear_rmsnorm_i8xi2(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma,
+                            float eps, const uint8_t* packed, const uint16_t* ws, int ws_num,
+                            const uint16_t* residual, uint16_t* y, uint16_t* xn_out,
+                            int8_t* q_out, float* s_out, int32_t* acc, int N, int K,
+                            hipStream_t stream);
+
+/*
  * Decode-step graph ([W2A8] §六 item 1: each decode step is a graph
  * replay).  A bl_gemv_desc is one M = 1 call of bitlinear_bf16_i8xi2; the
  * graph chains n of them in array order (each depends on the previous one)
@@ -231,6 +270,29 @@ typedef struct bl_graph bl_graph;
  * for an invalid descriptor, BL_ERR_HIP.
  */
 int bl_graph_create(const bl_gemv_desc* descs, int n, bl_graph** out);
+
+/*
+ * A decode step chained through its glue: each bl_norm_desc is one call of
+ * bitlinear_rmsnorm_i8xi2 (without the optional outputs); the graph runs
+ * them in array order, so a call may read what an earlier one wrote (its
+ * x, x_up or residual may be an earlier y).  Same rules and errors as
+ * bl_graph_create, with bitlinear_rmsnorm_i8xi2's checks per descriptor.
+ */
+typedef struct bl_norm_desc {
+    const uint16_t* x;        /* device, bf16, K */
+    const uint16_t* x_up;     /* device, bf16, K, or NULL */
+    const uint16_t* gamma;    /* device, bf16, K */
+    float eps;
+    const uint8_t* packed;    /* device, bl_packed_bytes(N, K) */
+    const uint16_t* ws;       /* device, bf16, ws_num */
+    int ws_num;
+    const uint16_t* residual; /* device, bf16, N, or NULL */
+    uint16_t* y;              /* device, bf16, N */
+    int N;
+    int K;
+} bl_norm_desc;
+
+int bl_graph_create_norm(const bl_norm_desc* descs, int n, bl_graph** out);
 
 /* Enqueue one replay of the graph on `stream`.  Errors: BL_ERR_NULL, BL_ERR_HIP. */
 int bl_graph_launch(bl_graph* graph, hipStream_t stream);

@@ -353,3 +353,23 @@ def norm_bitlinear(x_bits, g_bits, w, ws_bits, ws_num, up_bits=None, residual_bi
     if residual_bits is not None:
         y = add_bf16(residual_bits, y)
     return xn, q.reshape(-1), s, acc.reshape(-1), y
+
+
+def chained_layer(w, ws_bits, ws_num, gamma, attn_out_bits, h_bits, eps=RMS_EPS):
+    """One layer of the decode step chained through its glue (the attention itself excluded;
+    ``attn_out_bits`` stands for its output):
+        qkv = wqkv(RMSNorm_attn(h))
+        h1  = h + wo(RMSNorm_attn_sub(attn_out))
+        gu  = w13(RMSNorm_ffn(h1))                       (gate half, then up half)
+        h2  = h1 + w2(RMSNorm_ffn_sub(relu(gate)^2 * up))
+    ``w``, ``ws_bits``, ``ws_num`` are keyed by qkv / o / gate_up / down and ``gamma`` by
+    attn / attn_sub / ffn / ffn_sub.  Returns dict(qkv, h1, gu, h2) of bf16 bits."""
+    qkv = norm_bitlinear(h_bits, gamma["attn"], w["qkv"], ws_bits["qkv"], ws_num["qkv"], eps=eps)[4]
+    h1 = norm_bitlinear(attn_out_bits, gamma["attn_sub"], w["o"], ws_bits["o"], ws_num["o"],
+                        residual_bits=h_bits, eps=eps)[4]
+    gu = norm_bitlinear(h1, gamma["ffn"], w["gate_up"], ws_bits["gate_up"], ws_num["gate_up"],
+                        eps=eps)[4]
+    half = gu.size // 2
+    h2 = norm_bitlinear(gu[:half], gamma["ffn_sub"], w["down"], ws_bits["down"], ws_num["down"],
+                        up_bits=gu[half:], residual_bits=h1, eps=eps)[4]
+    return {"qkv": qkv, "h1": h1, "gu": gu, "h2": h2}

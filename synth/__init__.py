@@ -24,6 +24,9 @@ import numpy as np
 
 BASE_SEED = 20261202
 
+# Model width and MLP width of the pages' 2B configuration (dim 2560, intermediate 6912).
+DIM = 2560
+FFN = 6912
 # (name, N, K, ws_num) of one transformer layer of the 2B-style model.
 LAYER_SET: List[Tuple[str, int, int, int]] = [
     ("qkv", 3840, 2560, 1),
@@ -185,3 +188,43 @@ def decode_step_nodes(n_layers: int = N_LAYERS) -> List[GemvF]:
             nodes.append(make_float_gemv(f"L{layer_i}.{n}", 1, N, K, wn,
                                          seed_for(5, layer_i, i), bf16=True))
     return nodes
+
+
+# --------------------------------------------------------------------------
+# Chained decode step: one block's projections joined through the model's
+# norms, MLP activation and residuals.  The attention itself is out of scope:
+# each layer's attention output is a seeded bf16 N(0, 1) row, and the qkv
+# projection's output is computed but feeds nothing.
+# --------------------------------------------------------------------------
+
+CHAIN_NORMS = ("attn", "attn_sub", "ffn", "ffn_sub")
+
+
+@dataclass
+class ChainLayer:
+    w: dict          # projection name (LAYER_SET names) -> int8 ternary N x K
+    ws: dict         # name -> bf16 bits [ws_num]
+    ws_num: dict     # name -> int
+    gamma: dict      # norm name (CHAIN_NORMS) -> bf16 bits [K of its input]
+    attn_out: np.ndarray   # bf16 bits [dim]: the attention output this layer's o reads
+
+
+def chained_layer(layer: int) -> ChainLayer:
+    """Weights (uniform ternary), weight scales, RMSNorm weights ~ N(1, 0.1) and the
+    attention output of one layer of the chained decode step."""
+    w, ws, wn = {}, {}, {}
+    for i, (name, N, K, ws_num) in enumerate(LAYER_SET):
+        g = rng(seed_for(6, layer, i))
+        w[name] = ternary_uniform(g, N, K)
+        ws[name] = ws_bits(g, ws_num)
+        wn[name] = ws_num
+    g = rng(seed_for(6, layer, 7))
+    dims = {"attn": DIM, "attn_sub": DIM, "ffn": DIM, "ffn_sub": FFN}
+    gamma = {k: _top16((1.0 + 0.1 * g.standard_normal(dims[k])).astype(np.float32)) for k in CHAIN_NORMS}
+    attn = normal_bf16_bits(g, 1, DIM).reshape(-1)
+    return ChainLayer(w, ws, wn, gamma, attn)
+
+
+def chained_h0() -> np.ndarray:
+    """The residual stream entering the first layer: bf16 N(0, 1) bits [dim]."""
+    return normal_bf16_bits(rng(seed_for(6, 99, 0)), 1, DIM).reshape(-1)

@@ -152,3 +152,45 @@ def test_graph_errors():
     assert lib.bl_graph_size(None) == bl.BL_ERR_NULL
     assert lib.bl_graph_destroy(None) == bl.BL_OK
     assert bl.status_string(bl.BL_ERR_ALIGN).startswith("a pointer")
+
+
+def _nrm(x=A, x_up=None, gamma=A, eps=1e-5, packed=A, ws=A, ws_num=1, res=None, y=A, xn=None,
+         q=None, s=None, acc=None, N=64, K=64):
+    return bl.lib().bitlinear_rmsnorm_i8xi2(x, x_up, gamma, eps, packed, ws, ws_num, res, y, xn,
+                                            q, s, acc, N, K, None)
+
+
+def test_rmsnorm_entry_errors():
+    assert _nrm(x=None) == bl.BL_ERR_NULL
+    assert _nrm(gamma=None) == bl.BL_ERR_NULL
+    assert _nrm(packed=None) == bl.BL_ERR_NULL
+    assert _nrm(ws=None) == bl.BL_ERR_NULL
+    assert _nrm(y=None) == bl.BL_ERR_NULL
+    assert _nrm(N=0) == bl.BL_ERR_SHAPE
+    assert _nrm(K=40) == bl.BL_ERR_SHAPE                 # K % 16 != 0
+    assert _nrm(K=32768 + 16) == bl.BL_ERR_SHAPE         # beyond the glue kernel's K
+    assert _nrm(eps=-1.0) == bl.BL_ERR_ARG
+    assert _nrm(eps=float("nan")) == bl.BL_ERR_ARG
+    assert _nrm(eps=float("inf")) == bl.BL_ERR_ARG
+    assert _nrm(ws_num=3, N=64) == bl.BL_ERR_ARG
+    assert _nrm(x=A + 8) == bl.BL_ERR_ALIGN
+    assert _nrm(x_up=A + 8) == bl.BL_ERR_ALIGN
+    assert _nrm(gamma=A + 2) == bl.BL_ERR_ALIGN
+    assert _nrm(res=U) == bl.BL_ERR_ALIGN
+    assert _nrm(xn=A + 8) == bl.BL_ERR_ALIGN
+    assert _nrm(q=A + 4) == bl.BL_ERR_ALIGN
+    assert _nrm(s=A + 2) == bl.BL_ERR_ALIGN
+
+
+def test_chained_graph_errors():
+    g = ctypes.c_void_p()
+    lib = bl.lib()
+    assert lib.bl_graph_create_norm(None, 1, ctypes.byref(g)) == bl.BL_ERR_NULL
+    arr = (bl.bl_norm_desc * 1)()
+    arr[0] = bl.bl_norm_desc(A, None, A, 1e-5, A, A, 1, None, A, 64, 64)
+    assert lib.bl_graph_create_norm(arr, 0, ctypes.byref(g)) == bl.BL_ERR_ARG
+    arr[0] = bl.bl_norm_desc(A, None, A, 1e-5, A, A, 1, None, A, 64, 40)
+    assert lib.bl_graph_create_norm(arr, 1, ctypes.byref(g)) == bl.BL_ERR_SHAPE
+    arr[0] = bl.bl_norm_desc(A, None, None, 1e-5, A, A, 1, None, A, 64, 64)
+    assert lib.bl_graph_create_norm(arr, 1, ctypes.byref(g)) == bl.BL_ERR_NULL
+    assert g.value is None

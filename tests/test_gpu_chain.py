@@ -1,0 +1,183 @@
+"""GPU parity of the decode step chained through its glue (bitlinear_rmsnorm_i8xi2 and
+bl_graph_create_norm) against the oracle.
+
+Each projection of the pages' 2B layer with the glue it takes in the chain -- qkv
+after attention_norm, o after attn_sub_norm plus the residual, gate+up after ffn_norm,
+down after relu(gate)^2 * up and ffn_sub_norm plus the residual -- compared output by
+output: the normalised row, its int8 quantisation and scale, the int32 accumulators and
+the bf16 result.  Then rows that are not multiples of the kernel's tiles, the smallest K,
+a zero row, a large-magnitude row, eps = 0, and a two-layer chain replayed as one graph.
+The normalised row is defined in fp64; the kernel's sum of squares runs in another order,
+so the bar is 1 ulp, but on these seeded inputs every value is expected to match exactly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import dev, bf16_dev, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bl():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import bit_gemv_bitlinear_amd as m
+    return m
+
+
+def run_proj(bl, x, gamma, w, ws, ws_num, x_up=None, residual=None, eps=oracle.RMS_EPS):
+    import torch
+    N, K = w.shape
+    packed = bl.pack_ternary_weights(dev(w))
+    xn = torch.empty((K,), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((K,), dtype=torch.int8, device="cuda")
+    s = torch.empty((1,), dtype=torch.float32, device="cuda")
+    acc = torch.empty((N,), dtype=torch.int32, device="cuda")
+    y = bl.bitlinear_rmsnorm_i8xi2(bf16_dev(x), packed, bf16_dev(gamma), bf16_dev(ws), N, ws_num,
+                                   x_up=None if x_up is None else bf16_dev(x_up),
+                                   residual=None if residual is None else bf16_dev(residual),
+                                   eps=eps, xn_out=xn, q_out=q, s_out=s, acc=acc)
+    torch.cuda.synchronize()
+    return host_bits(xn), q.cpu().numpy(), s.cpu().numpy(), acc.cpu().numpy(), host_bits(y)
+
+
+def check_proj(bl, name, x, gamma, w, ws, ws_num, x_up=None, residual=None, eps=oracle.RMS_EPS):
+    print(f"chain projection {name}: N={w.shape[0]} K={w.shape[1]} glu={x_up is not None} "
+          f"residual={residual is not None}", flush=True)
+    got = run_proj(bl, x, gamma, w, ws, ws_num, x_up, residual, eps)
+    want = oracle.norm_bitlinear(x, gamma, w, ws, ws_num, up_bits=x_up, residual_bits=residual,
+                                 eps=eps)
+    for label, g_, w_ in zip(("xn", "q", "s", "acc", "y"), got, want):
+        np.testing.assert_array_equal(np.asarray(g_).reshape(-1), np.asarray(w_).reshape(-1),
+                                      err_msg=f"{name}: {label}")
+
+
+@pytest.mark.parametrize("proj", ["qkv", "o", "gate_up", "down"])
+def test_model_projection_with_glue(bl, proj):
+    L = synth.chained_layer(0)
+    h = synth.chained_h0()
+    g = synth.rng(4242)
+    if proj == "qkv":
+        check_proj(bl, proj, h, L.gamma["attn"], L.w["qkv"], L.ws["qkv"], 1)
+    elif proj == "o":
+        check_proj(bl, proj, L.attn_out, L.gamma["attn_sub"], L.w["o"], L.ws["o"], 1, residual=h)
+    elif proj == "gate_up":
+        check_proj(bl, proj, h, L.gamma["ffn"], L.w["gate_up"], L.ws["gate_up"], 2)
+    else:
+        gate = synth.normal_bf16_bits(g, 1, synth.FFN).reshape(-1)
+        up = synth.normal_bf16_bits(g, 1, synth.FFN).reshape(-1)
+        check_proj(bl, proj, gate, L.gamma["ffn_sub"], L.w["down"], L.ws["down"], 1, x_up=up,
+                   residual=h)
+
+
+# (6400, 2320) and (16, 28688): rows longer than the chunks a thread caches,
+# so the kernel's loop over uncached chunks runs
+@pytest.mark.parametrize("N,K,ws_num,glu", [(100, 272, 2, False), (16, 16, 1, True),
+                                            (1000, 4096, 4, True), (8200, 512, 1, False),
+                                            (6400, 2320, 2, True), (16, 28688, 1, False)])
+def test_ragged_shapes(bl, N, K, ws_num, glu):
+    g = synth.rng(N + K)
+    x = synth.normal_bf16_bits(g, 1, K).reshape(-1)
+    up = synth.normal_bf16_bits(g, 1, K).reshape(-1) if glu else None
+    gamma = synth._top16((1.0 + 0.1 * g.standard_normal(K)).astype(np.float32))
+    w = synth.ternary_uniform(g, N, K)
+    res = synth.normal_bf16_bits(g, 1, N).reshape(-1)
+    check_proj(bl, f"ragged{N}x{K}", x, gamma, w, synth.ws_bits(g, ws_num), ws_num, x_up=up,
+               residual=res)
+
+
+def test_zero_and_large_rows_and_no_eps(bl):
+    g = synth.rng(31)
+    K, N = 2560, 2560
+    w = synth.ternary_uniform(g, N, K)
+    ws = synth.ws_bits(g, 1)
+    gamma = synth._top16((1.0 + 0.1 * g.standard_normal(K)).astype(np.float32))
+    res = synth.normal_bf16_bits(g, 1, N).reshape(-1)
+    zero = np.zeros(K, dtype=np.uint16)
+    check_proj(bl, "zero row", zero, gamma, w, ws, 1, residual=res)            # y = residual
+    big = synth._top16((1e30 * g.standard_normal(K)).astype(np.float32))
+    check_proj(bl, "large row", big, gamma, w, ws, 1)
+    x = synth.normal_bf16_bits(g, 1, K).reshape(-1)
+    check_proj(bl, "eps 0", x, gamma, w, ws, 1, eps=0.0)
+    neg = synth._top16(-np.abs(g.standard_normal(K)).astype(np.float32))       # GLU gate <= 0
+    check_proj(bl, "negative gate", neg, gamma, w, ws, 1, x_up=x, residual=res)
+
+
+def test_rounding_extremes(bl):
+    # values whose roundings land among bf16's subnormals or far from 1
+    g = synth.rng(47)
+    K, N = 2560, 2560
+    w = synth.ternary_uniform(g, N, K)
+    ws = synth.ws_bits(g, 1)
+    x = synth.normal_bf16_bits(g, 1, K).reshape(-1)
+    gamma_sub = synth._top16((1e-39 * g.standard_normal(K)).astype(np.float32))   # subnormal gamma
+    check_proj(bl, "subnormal gamma", x, gamma_sub, w, ws, 1)
+    gamma = synth._top16(g.standard_normal(K).astype(np.float32))                  # signed gamma
+    tiny_gate = synth._top16((1e-20 * g.standard_normal(K)).astype(np.float32))    # m subnormal
+    check_proj(bl, "subnormal GLU", tiny_gate, gamma, w, ws, 1, x_up=x)
+    big_gate = synth._top16((1e15 * g.standard_normal(K)).astype(np.float32))
+    big_up = synth._top16((1e5 * g.standard_normal(K)).astype(np.float32))
+    check_proj(bl, "large GLU", big_gate, gamma, w, ws, 1, x_up=big_up)
+
+
+def test_bf16_midpoints(bl):
+    # normalised values that are exactly a bf16 midpoint (eps = 0), and values
+    # just below one whose nearest fp32 is the midpoint (eps = 2^-28): the
+    # oracle's pin test derives both by hand; repeated over a row of 2560
+    g = synth.rng(53)
+    K, N = 2560, 1024
+    w = synth.ternary_uniform(g, N, K)
+    ws = synth.ws_bits(g, 1)
+    x = np.tile(np.array([0x3FC0] * 4 + [0x3F80] * 7 + [0] * 5, dtype=np.uint16), K // 16)
+    gamma = np.full(K, 0x3F81, dtype=np.uint16)
+    check_proj(bl, "midpoint ties", x, gamma, w, ws, 1, eps=0.0)
+    check_proj(bl, "below midpoints", x, gamma, w, ws, 1, eps=np.float32(2.0 ** -28))
+
+
+def test_chained_two_layers_as_graph(bl):
+    import torch
+    n_layers = 2
+    layers = [synth.chained_layer(l) for l in range(n_layers)]
+    h0 = synth.chained_h0()
+    print("chained graph: 2 layers x 4 projections", flush=True)
+    dim, ffn = synth.DIM, synth.FFN
+    h = [bf16_dev(h0)] + [torch.empty(dim, dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
+    calls, keep, outs = [], [], []
+    for l, L in enumerate(layers):
+        p = {k: bl.pack_ternary_weights(dev(v)) for k, v in L.w.items()}
+        wsd = {k: bf16_dev(v) for k, v in L.ws.items()}
+        gm = {k: bf16_dev(v) for k, v in L.gamma.items()}
+        a = bf16_dev(L.attn_out)
+        qkv = torch.empty(3840, dtype=torch.bfloat16, device="cuda")
+        h1 = torch.empty(dim, dtype=torch.bfloat16, device="cuda")
+        gu = torch.empty(2 * ffn, dtype=torch.bfloat16, device="cuda")
+        keep += [p, wsd, gm, a]
+        outs.append({"qkv": qkv, "h1": h1, "gu": gu, "h2": h[l + 1]})
+        calls += [
+            dict(x=h[l], gamma=gm["attn"], packed=p["qkv"], ws=wsd["qkv"], ws_num=1, y=qkv, N=3840, K=dim),
+            dict(x=a, gamma=gm["attn_sub"], packed=p["o"], ws=wsd["o"], ws_num=1, residual=h[l], y=h1,
+                 N=dim, K=dim),
+            dict(x=h1, gamma=gm["ffn"], packed=p["gate_up"], ws=wsd["gate_up"], ws_num=2, y=gu,
+                 N=2 * ffn, K=dim),
+            dict(x=gu[:ffn], x_up=gu[ffn:], gamma=gm["ffn_sub"], packed=p["down"], ws=wsd["down"],
+                 ws_num=1, residual=h1, y=h[l + 1], N=dim, K=ffn),
+        ]
+    graph = bl.ChainedDecodeGraph(calls)
+    assert len(graph) == 4 * n_layers
+    # oracle chain
+    want, hb = [], h0
+    for L in layers:
+        r = oracle.chained_layer(L.w, L.ws, L.ws_num, L.gamma, L.attn_out, hb)
+        want.append(r)
+        hb = r["h2"]
+    for rep in range(3):   # replays with host synchronisation between them
+        graph.launch()
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            for k in ("qkv", "h1", "gu", "h2"):
+                np.testing.assert_array_equal(host_bits(outs[l][k]), want[l][k],
+                                              err_msg=f"replay {rep} layer {l} {k}")
+    graph.close()

@@ -186,3 +186,19 @@ def test_add_against_exact():
         else:
             want.append(bf16_bits_of_exact(v))
     np.testing.assert_array_equal(oracle.add_bf16(a, b), np.array(want, dtype=np.uint16))
+
+
+def test_rmsnorm_midpoint_closed_form():
+    # K = 16: four values 1.5, seven 1.0, five 0 -> sum of squares 16, mean 1;
+    # gamma = 129/128.  With eps = 0, inv = 1 and 1.5 * 129/128 = 193.5/128 is
+    # a bf16 midpoint: ties to even -> 194/128 (0x3FC2).  With eps = 2^-28,
+    # inv = 1/sqrt(1 + 2^-28) sits just below 1, so the value falls just below
+    # the midpoint -> 193/128 (0x3FC1), although its nearest fp32 is the
+    # midpoint itself (a rounding through fp32 would give 0x3FC2).  The ones
+    # give 129/128 (0x3F81) either way.
+    x = np.array([0x3FC0] * 4 + [0x3F80] * 7 + [0] * 5, dtype=np.uint16)
+    g = np.full(16, 0x3F81, dtype=np.uint16)
+    want0 = np.array([0x3FC2] * 4 + [0x3F81] * 7 + [0] * 5, dtype=np.uint16)
+    want1 = np.array([0x3FC1] * 4 + [0x3F81] * 7 + [0] * 5, dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(x, g, eps=0.0), want0)
+    np.testing.assert_array_equal(oracle.rmsnorm_bf16(x, g, eps=np.float32(2.0 ** -28)), want1)
