@@ -42,7 +42,7 @@ A100_W2A8_GBS_13824x2560 = 473.5  # the page's 18.75 us on A100 (§7.1), as GB/s
 CACHE_DEFEAT_BYTES = 512 << 20
 PROFILE_PMC = os.path.join(ROOT, "profiles", "gemv_i8_13824x2560_pmc.txt")
 GEMV_SOURCES = [os.path.join(ROOT, "bit_gemv_bitlinear_amd", "csrc", f)
-                for f in ("gemv.hip", "common.hpp")]
+                for f in ("gemv.hip", "gemv_core.hpp", "common.hpp")]
 PROBE_LIB = os.path.join(ROOT, "bit_gemv_bitlinear_amd", "libstream_floor.so")
 
 

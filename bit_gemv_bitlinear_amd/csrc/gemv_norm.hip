@@ -1,0 +1,429 @@
+// gemv_norm.hip -- one projection of a decode step with the glue before it,
+// in one kernel on gfx950.  Source page: "BitNet GPU 推理框架：从零构建 W2A8 的
+// 2-bit 大模型 CUDA GEMV 内核" (blog.gitcode.com), cited as [W2A8].
+#include <algorithm>
+#include <array>
+#include <utility>
+
+#include "gemv_core.hpp"
+#include "kernels.hpp"
+
+namespace bl {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// The projection of a decode step with its glue ([W2A8] §4.1 names the
+// model's norms attention_norm / ffn_norm / attn_sub_norm / ffn_sub_norm and
+// its fused projections wqkv / wo / w13 / w2; the formulas are readings):
+//   m  = x, or bf16(max(x, 0)^2 * x_up) for the MLP's down projection
+//        (x = the gate half and x_up = the up half of w13's output);
+//   xn = bf16( fl64(m * gamma) * fl64(1 / sqrt(sum(m^2) / K + eps)) );
+//   per-token absmax int8 quantisation of xn, the ternary layer, and
+//   y = bf16(acc * ws / s), or bf16(residual + that) when a residual is given.
+// The glue runs in the prologue of every workgroup (the row is at most a few
+// thousand elements, read from L2 by each): no kernel of its own, so a chained
+// decode step launches one kernel per projection.  Everything else is the
+// staged kernel above: the weight loads are all issued before the first wait.
+// ---------------------------------------------------------------------------
+
+// Sum of a double over the 64 lanes: the two 32-bit halves move together
+// through the DPP steps of wave_sum (pairs, quads, rotations by 4 and 8 inside
+// each row of 16), then the four row totals are read out and added.  The
+// result is the same in every lane.
+template <int CTRL>
+__device__ __forceinline__ double dpp_row_f64(double v) {
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_row_f64<kDppQuadXor1>(v);
+    v += dpp_row_f64<kDppQuadXor2>(v);
+    v += dpp_row_f64<kDppRowRor4>(v);
+    v += dpp_row_f64<kDppRowRor8>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// Unsigned maximum over the 64 lanes, by the same steps.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_row_u32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_row_u32<kDppQuadXor1>(v));
+    v = max(v, dpp_row_u32<kDppQuadXor2>(v));
+    v = max(v, dpp_row_u32<kDppRowRor4>(v));
+    v = max(v, dpp_row_u32<kDppRowRor8>(v));
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+__device__ __forceinline__ uint32_t bf16_lo(uint32_t w) { return w & 0xFFFFu; }
+__device__ __forceinline__ uint32_t bf16_hi(uint32_t w) { return w >> 16; }
+__device__ __forceinline__ double bf16_f64(uint32_t b) {
+    return static_cast<double>(__uint_as_float(b << 16));
+}
+
+// bf16 rounding (nearest, ties to even) of an fp64 value in two hardware
+// steps: to fp32 rounded to odd, then fp32 to bf16 with ties to even.  An
+// intermediate format with at least two more significant bits than the
+// target makes that pair equal to one direct rounding (Boldo and Melquiond,
+// "Emulation of FMA and correctly rounded sums: proved algorithms using
+// rounding to odd", IEEE Trans. Computers 57(4), 2008); fp32 carries 24 bits
+// against bf16's 8, also among the subnormals (quantum 2^-149 against
+// 2^-133), and shares bf16's exponent range, so a value beyond it lands on
+// fp32's largest finite value, which rounds on to infinity as it should.
+// Rounding to odd: the nearest fp32 (the conversion's own rounding, ties to
+// even, with fp32 subnormals kept), and when that is inexact and even, its
+// neighbour on the other side of the value, which is odd.  NaN gives the
+// quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_rne_f64(double d) {
+    const float f = static_cast<float>(d);
+    uint32_t u = __float_as_uint(f);
+    const double back = static_cast<double>(f);
+    if (back != d && !(u & 1u)) u += fabs(back) > fabs(d) ? 0xFFFFFFFFu : 1u;
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return d != d ? 0x7FC0u : u;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed bf16 (a in the low half), nearest with ties to
+// even: v_cvt_pk_bf16_f32 in the default rounding mode.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Eight fp64 values to bf16 (nearest, ties to even) by way of fp32: one
+// conversion to fp32, one to bf16.  Every bf16 midpoint is an fp32 number,
+// so the first rounding can land on one but never step across one: the two
+// roundings differ from one direct rounding only where the fp32 value is a
+// bf16 midpoint (low 16 bits 0x8000).  Such chunks, and NaN, are rounded
+// again by bf16_rne_f64.
+__device__ __forceinline__ uint4 bf16x8_from_f64(const double (&d)[8]) {
+    uint32_t o[4];
+    bool redo = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float f0 = static_cast<float>(d[2 * j]), f1 = static_cast<float>(d[2 * j + 1]);
+        redo = redo | ((__float_as_uint(f0) & 0xFFFFu) == 0x8000u);
+        redo = redo | ((__float_as_uint(f1) & 0xFFFFu) == 0x8000u);
+        redo = redo | __builtin_isunordered(f0, f1);
+        o[j] = cvt_pk_bf16(f0, f1);
+    }
+    // a wave-uniform branch, taken by a wavefront when any of its lanes needs
+    // it (rarely); the empty volatile statement keeps the compiler from
+    // if-converting it, which would pay its work on every chunk
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+        asm volatile("");
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = bf16_rne_f64(d[2 * j]) | (bf16_rne_f64(d[2 * j + 1]) << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Chunk of 8 bf16: relu2-GLU, exact in fp64 (at most 24 significant bits),
+// rounded once, into m.
+__device__ __forceinline__ uint4 glu8(const uint4& g, const uint4& u) {
+    const uint32_t gd[4] = {g.x, g.y, g.z, g.w};
+    const uint32_t ud[4] = {u.x, u.y, u.z, u.w};
+    double m[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float a0 = __uint_as_float(gd[j] << 16), a1 = __uint_as_float(gd[j] & 0xFFFF0000u);
+        const double g0 = a0 > 0.0f ? static_cast<double>(a0) : 0.0;
+        const double g1 = a1 > 0.0f ? static_cast<double>(a1) : 0.0;
+        m[2 * j] = g0 * g0 * bf16_f64(bf16_lo(ud[j]));
+        m[2 * j + 1] = g1 * g1 * bf16_f64(bf16_hi(ud[j]));
+    }
+    return bf16x8_from_f64(m);
+}
+
+// p = m * gamma (exact in fp64) for a chunk of 8, with the running sum of
+// m^2 and the running maximum of |p| as the high word of its encoding: p has
+// at most 16 significant bits, all in that word (the low word is zero), so
+// comparing high words of magnitudes as integers compares the magnitudes.
+__device__ __forceinline__ void products8(const uint4& m, const uint4& g, double (&p)[8],
+                                          double& ssq, uint32_t& pm) {
+    const uint32_t md[4] = {m.x, m.y, m.z, m.w};
+    const uint32_t gd[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const double a = bf16_f64(bf16_lo(md[j])), b = bf16_f64(bf16_hi(md[j]));
+        p[2 * j] = a * bf16_f64(bf16_lo(gd[j]));
+        p[2 * j + 1] = b * bf16_f64(bf16_hi(gd[j]));
+        ssq += a * a;
+        ssq += b * b;
+        pm = max(pm, max(static_cast<uint32_t>(__double2hiint(p[2 * j])) & 0x7FFFFFFFu,
+                         static_cast<uint32_t>(__double2hiint(p[2 * j + 1])) & 0x7FFFFFFFu));
+    }
+}
+
+// xn = bf16(p * inv) for a chunk of 8 (NaN where inv is infinite and p zero:
+// a zero row with eps = 0).
+__device__ __forceinline__ uint4 norm8(const double (&p)[8], double inv) {
+    double v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = p[e] * inv;
+    return bf16x8_from_f64(v);
+}
+
+// A row of K bf16 values as a raw buffer (16-byte loads by chunk index).
+using RowBuf = __amdgpu_buffer_rsrc_t;
+constexpr int kRawBufferFlags = 0x00020000;   // word 3 of the descriptor: 32-bit data format
+__device__ __forceinline__ RowBuf row_buffer(const uint16_t* p, int K) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, 2 * K, kRawBufferFlags);
+}
+__device__ __forceinline__ uint4 row_load(RowBuf r, int chunk) {
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, chunk * 16, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// At most kNormMaxWaves wavefronts per workgroup: the registers that hold
+// the row's exact products (two per value) need the larger per-wavefront
+// budget.
+constexpr int kNormMaxWaves = 8;
+
+template <int P, int C, bool GLU>
+__global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ x_up,
+    const uint16_t* __restrict__ gamma, double eps, const v4u* __restrict__ packed,
+    const uint16_t* __restrict__ ws, uint32_t seg_mul, int seg_shift,
+    const uint16_t* __restrict__ residual, uint16_t* __restrict__ y, int32_t* __restrict__ acc,
+    int8_t* __restrict__ q_out, float* __restrict__ s_out, uint16_t* __restrict__ xn_out, int N,
+    int K, int B, int lw) {
+    extern __shared__ int4 act[];   // Wb*P*16 16-byte chunks: the int8 row, zero-padded
+    __shared__ int part_sh[kNormMaxWaves][64];
+    __shared__ int xsum_sh[kNormMaxWaves];
+    __shared__ double ssq_sh[kNormMaxWaves];
+    __shared__ uint32_t pm_sh[kNormMaxWaves];
+    const int Wb = 1 << lw;
+    const int W = B << lw;
+    const int nthreads = W * 64;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nbands = (N + kTileRows - 1) / kTileRows;
+    const int band = min(static_cast<int>(blockIdx.x) * B + (wave >> lw), nbands - 1);
+    const int S = (K + kTileK - 1) / kTileK;
+    const int s0 = (wave & (Wb - 1)) * P;
+    const int n16 = K >> 4;
+    const int padded16 = Wb * P * 16;
+    const int n_in = K >> 3;        // 16-byte chunks of bf16
+
+    // 1. The inputs of this thread's output row (weight scale, residual),
+    //    the cached chunks of the row (x, x_up, gamma), then every weight load.
+    const int n_out = static_cast<int>(blockIdx.x) * B * kTileRows + tid;   // tid < 16*B writes
+    const uint32_t n_c = static_cast<uint32_t>(min(n_out, N - 1));
+    const uint16_t wsb = ws[(static_cast<uint64_t>(n_c) * seg_mul) >> seg_shift];
+    // unconditional (a branch would end in a wait for this load); the weight
+    // scales stand in as a source when there is no residual
+    const uint16_t resb = (residual ? residual : ws)[residual ? n_c : 0u];
+    const uint4* x16 = reinterpret_cast<const uint4*>(x);
+    const uint4* u16 = reinterpret_cast<const uint4*>(x_up);
+    const uint4* g16 = reinterpret_cast<const uint4*>(gamma);
+    // The cached chunks come through buffer loads: the compiler treats plain
+    // loads of these read-only rows as free to sink to their first use,
+    // past the weight loads, and a wait there would wait for every one.
+    const RowBuf rx = row_buffer(x, K), ru = row_buffer(x_up, K), rg = row_buffer(gamma, K);
+    // A chunk past the row's end reads as zeros (the buffer's range check),
+    // which add nothing to the sum of squares or the maximum.
+    uint4 xv[C], uv[GLU ? C : 1], gv[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int idx = tid + c * nthreads;
+        xv[c] = row_load(rx, idx);
+        if constexpr (GLU) uv[c] = row_load(ru, idx);
+        gv[c] = row_load(rg, idx);
+    }
+    const v4u* tiles = packed + static_cast<size_t>(band) * S * 64 + lane;
+    v4u w[P];
+    load_steps<P>(tiles, s0, S - 1, w);
+    // No load may move below this point (a row load sunk past the weight
+    // loads would wait for all of them: the waits count loads in issue
+    // order), and nothing may be scheduled above it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. m (GLU); p = m * gamma, exact in fp64 and kept for step 4; the sum
+    //    of m^2 and the largest |p|.  Chunks beyond the C cached ones (rows
+    //    longer than C x 8 x threads) are re-read from L2, here and in step 4.
+    auto m_chunk = [&](int c, int idx) -> uint4 {
+        if (c < C) {
+            if constexpr (GLU) return glu8(xv[c], uv[c]);
+            return xv[c];
+        }
+        if constexpr (GLU) return glu8(x16[idx], u16[idx]);
+        return x16[idx];
+    };
+    double ssq = 0.0;
+    uint32_t pm = 0;   // high word of the largest |p|
+    double pv[C][8];
+#pragma unroll
+    for (int c = 0; c < C; ++c) products8(m_chunk(c, tid + c * nthreads), gv[c], pv[c], ssq, pm);
+    for (int idx = tid + C * nthreads; idx < n_in; idx += nthreads) {
+        double pt[8];
+        products8(m_chunk(C, idx), g16[idx], pt, ssq, pm);
+    }
+    ssq = wave_sum_f64(ssq);
+    pm = wave_max_u32(pm);
+    if (lane == 0) {
+        ssq_sh[wave] = ssq;
+        pm_sh[wave] = pm;
+    }
+    __syncthreads();
+
+    // 3. The inverse RMS and the activation scale.  Rounding is monotone and
+    //    inv > 0, so the largest |xn| is the bf16 rounding of pmax * inv: the
+    //    absmax needs no pass over xn.  The partial sums are added in wave
+    //    order; all eight slots are read at once and the unused ones dropped.
+    double total_sq = 0.0;
+    pm = 0;
+#pragma unroll
+    for (int i = 0; i < kNormMaxWaves; ++i) {
+        const double v = ssq_sh[i];
+        const uint32_t u = pm_sh[i];
+        total_sq += i < W ? v : 0.0;
+        pm = max(pm, i < W ? u : 0u);
+    }
+    const double inv = 1.0 / sqrt(total_sq / static_cast<double>(K) + eps);
+    const double pmax = __hiloint2double(static_cast<int>(pm), 0);
+    const float amax = __uint_as_float(bf16_rne_f64(pmax * inv) << 16);
+    const float sm = 127.0f / fmaxf(amax, 1e-5f);
+
+    // 4. Quantise xn into LDS (workgroup 0 also writes xn, q and s when asked).
+    uint2* act8 = reinterpret_cast<uint2*>(act);
+    const bool first = blockIdx.x == 0;
+    int xs = 0;
+    auto put = [&](int idx, const uint4& v) {
+        const uint2 o = quant8_bf16(v, sm);
+        act8[idx] = o;
+        xs = sum_i8x4(o.x, sum_i8x4(o.y, xs));
+        if (first && q_out) reinterpret_cast<uint2*>(q_out)[idx] = o;
+        if (first && xn_out) reinterpret_cast<uint4*>(xn_out)[idx] = v;
+    };
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int idx = tid + c * nthreads;
+        if (idx < n_in) put(idx, norm8(pv[c], inv));
+    }
+    for (int idx = tid + C * nthreads; idx < n_in; idx += nthreads) {
+        double pt[8];
+        products8(m_chunk(C, idx), g16[idx], pt, ssq, pm);
+        put(idx, norm8(pt, inv));
+    }
+    if (first && s_out != nullptr && tid == 0) s_out[0] = sm;
+    for (int i = n16 + tid; i < padded16; i += nthreads) act[i] = make_int4(0, 0, 0, 0);
+    xs = wave_sum(xs);
+    if (lane == 0) xsum_sh[wave] = xs;
+    __syncthreads();
+    double cs = 0.0;
+    int offset = 0;
+    if (wave == 0) {
+        cs = static_cast<double>(bf16_to_float(wsb)) * (1.0 / static_cast<double>(sm));
+        for (int i = 0; i < W; ++i) offset -= 2 * xsum_sh[i];
+        asm volatile("" : "+v"(cs), "+v"(offset));
+    }
+
+    // 5. P steps of 4 rows x 16 K per lane, reduction, epilogue (+ residual).
+    RowAcc r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.a1[i] = r.a4[i] = r.a16[i] = 0;
+    const int kc = lane & 15;
+#pragma unroll
+    for (int u = 0; u < P; ++u) dot_slot(w[u], act[(s0 + u) * 16 + kc], r);
+    int v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = r.a1[i] + (r.a4[i] >> 2) + (r.a16[i] >> 4);
+    part_sh[wave][lane] = row_group_reduce(v, lane);
+    __syncthreads();
+    if (wave == 0) {
+        const int bw = lane >> 4;
+        const int rw = lane & 15;
+        const int slot = 16 * (rw >> 2) + (rw & 3);
+        const int firstw = min(bw, B - 1) << lw;
+        int total = offset;
+        for (int j = 0; j < Wb; ++j) total += part_sh[firstw + j][slot];
+        if (bw < B && n_out < N) {
+            uint16_t o = epilogue_bf16_scaled(total, cs, bf16_to_float(wsb), sm);
+            if (residual)   // the fp64 sum of two bf16 values rounds to bf16 as the exact sum does
+                o = static_cast<uint16_t>(bf16_rne_f64(static_cast<double>(bf16_to_float(resb)) +
+                                                       static_cast<double>(bf16_to_float(o))));
+            y[n_out] = o;
+            if (acc) acc[n_out] = total;
+        }
+    }
+}
+
+using GemvNormFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, double, const v4u*,
+                            const uint16_t*, uint32_t, int, const uint16_t*, uint16_t*, int32_t*,
+                            int8_t*, float*, uint16_t*, int, int, int, int);
+template <int C, bool GLU, int... Ps>
+constexpr std::array<GemvNormFn, sizeof...(Ps)> norm_table(std::integer_sequence<int, Ps...>) {
+    return {{&gemv_norm_kernel<Ps + 1, C, GLU>...}};
+}
+// P = 1 .. kNormMaxSteps (rows up to kNormMaxK over at most kNormMaxWaves
+// wavefronts per band) and C = 1 or 2 cached chunks per thread; the loop over
+// uncached chunks serves longer rows.
+constexpr int kNormMaxSteps = 16;
+using NormRow = std::array<GemvNormFn, kNormMaxSteps>;
+// [glu][C - 1][P - 1]
+const std::array<std::array<NormRow, 2>, 2> kNormKernels = {{
+    {{norm_table<1, false>(std::make_integer_sequence<int, kNormMaxSteps>{}),
+      norm_table<2, false>(std::make_integer_sequence<int, kNormMaxSteps>{})}},
+    {{norm_table<1, true>(std::make_integer_sequence<int, kNormMaxSteps>{}),
+      norm_table<2, true>(std::make_integer_sequence<int, kNormMaxSteps>{})}},
+}};
+
+// The geometry of gemv_shape with at most kNormMaxWaves wavefronts per
+// workgroup: fewer wavefronts per band (longer runs) or fewer bands.
+GemvShape norm_shape(int N, int K) {
+    const int S = (K + kTileK - 1) / kTileK;
+    const int nbands = (N + kTileRows - 1) / kTileRows;
+    const int target = nbands < kNarrowBands ? kTargetStepsNarrow : kTargetSteps;
+    int Wb = 1;
+    while (Wb < kNormMaxWaves && (S + Wb - 1) / Wb > target) Wb <<= 1;
+    const int P = (S + Wb - 1) / Wb;
+    if (P > kNormMaxSteps) return GemvShape{0, 0, 0};
+    int B = 4;
+    while (B > 1 && (nbands / B < kMinGroups || B * Wb > kNormMaxWaves)) B >>= 1;
+    return GemvShape{B * Wb, P, B};
+}
+
+}  // namespace
+
+hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma,
+                            float eps, const uint8_t* packed, const uint16_t* ws, int ws_num,
+                            const uint16_t* residual, uint16_t* y, uint16_t* xn_out,
+                            int8_t* q_out, float* s_out, int32_t* acc, int N, int K,
+                            hipStream_t stream) {
+    const GemvShape g = norm_shape(N, K);
+    if (g.waves == 0 || K > kNormMaxK) return hipErrorInvalidValue;
+    const int nbands = (N + kTileRows - 1) / kTileRows;
+    const unsigned groups = static_cast<unsigned>((nbands + g.bands - 1) / g.bands);
+    const int wb = g.waves / g.bands;
+    int lw = 0;
+    while ((1 << lw) < wb) ++lw;
+    const size_t lds = static_cast<size_t>(wb) * g.steps * kTileK;
+    const int threads = g.waves * 64;
+    const int need = (K / 8 + threads - 1) / threads;
+    const GemvNormFn fn = kNormKernels[x_up ? 1 : 0][need <= 1 ? 0 : 1][g.steps - 1];
+    uint32_t seg_mul;
+    int seg_shift;
+    seg_divisor(N / ws_num, seg_mul, seg_shift);
+    fn<<<groups, threads, lds, stream>>>(x, x_up, gamma, static_cast<double>(eps),
+                                         reinterpret_cast<const v4u*>(packed), ws, seg_mul,
+                                         seg_shift, residual, y, acc, q_out, s_out, xn_out, N, K,
+                                         g.bands, lw);
+    return hipGetLastError();
+}
+
+}  // namespace bl

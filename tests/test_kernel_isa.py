@@ -38,6 +38,11 @@ def gemv_asm(tmp_path_factory):
 
 
 @pytest.fixture(scope="module")
+def norm_asm(tmp_path_factory):
+    return _asm(tmp_path_factory, "gemv_norm.hip")
+
+
+@pytest.fixture(scope="module")
 def mfma_asm(tmp_path_factory):
     return _asm(tmp_path_factory, "gemm_mfma.hip")
 
@@ -148,20 +153,20 @@ def test_prefill_no_scratch_and_declared_lds(prefill_asm):
         assert body.count("v_mfma_i32_16x16x64_i8") == 16 * MTW, name
 
 
-def test_norm_kernels_issue_all_loads_first(gemv_asm):
+def test_norm_kernels_issue_all_loads_first(norm_asm):
     # gemv_norm_kernel<P, C, GLU>: the row's C chunks of x, gamma (and x_up),
     # buffer loads, and all P weight tiles are issued before the first wait,
     # without scratch
-    kernels = list(re.finditer(r"^(_ZN\S*gemv_norm_kernelILi(\d+)ELi(\d)ELb([01])E\S*):", gemv_asm, re.M))
+    kernels = list(re.finditer(r"^(_ZN\S*gemv_norm_kernelILi(\d+)ELi(\d)ELb([01])E\S*):", norm_asm, re.M))
     assert len(kernels) == 64    # P = 1..16, C = 1, 2, with and without the GLU
     late = []
     for m in kernels:
         name, P, C, glu = m.group(1), int(m.group(2)), int(m.group(3)), m.group(4) == "1"
-        body = gemv_asm[m.end():gemv_asm.index("s_endpgm", m.end())]
+        body = norm_asm[m.end():norm_asm.index("s_endpgm", m.end())]
         first_wait = body.index("s_waitcnt vmcnt")
         weights = len(re.findall(r"global_load_dwordx4 [^\n]* nt\b", body[:first_wait]))
         rows = len(re.findall(r"buffer_load_dwordx4 ", body[:first_wait]))
         if weights != P or rows != C * (3 if glu else 2):
             late.append((P, C, glu, weights, rows))
-        assert _meta(gemv_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
+        assert _meta(norm_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
     assert not late, f"(P, C, glu, weight loads, row loads before the first wait): {late}"
