@@ -66,7 +66,7 @@ namespace {
 // FUSED = false: xin is int8 activations with scale s_in[0].
 // FUSED = true:  xin is bf16; the workgroup quantises it (per-token absmax,
 //                [W2A8] §六 item 3); workgroup 0 writes q_out / s_out if given.
-template <int P, bool FUSED, int C>
+template <int P, bool FUSED, int C, bool OWN>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     const void* __restrict__ xin, const v4u* __restrict__ packed, const float* __restrict__ s_in,
     const uint16_t* __restrict__ ws, uint32_t seg_mul, int seg_shift, uint16_t* __restrict__ y,
@@ -92,7 +92,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     // 1. The activation row and the weight scale of this thread's output row
     //    first (so that waiting for them does not wait for the weights), then
     //    every weight load of this wavefront.
-    const int n_out = static_cast<int>(blockIdx.x) * B * kTileRows + tid;   // tid < 16*B writes
+    // OWN (one wavefront per band, Wb = 1): each wavefront finishes its own
+    // band, without the last barrier: lane l with (l / 4) % 4 == 0 writes row
+    // 4 * (l / 16) + l % 4, where the row reduction leaves that row's sum.
+    // Otherwise wavefront 0 writes row tid of the workgroup's bands after a
+    // barrier.  Measured same-box at 13824 x 2560 with int8 input: 3.60 ->
+    // 3.54 us; with bf16 input every wavefront's ws / s, formed after the
+    // quantisation, lengthens the path to the main loop (3.65 -> 3.76 us),
+    // so the fused kernels keep the barrier.
+    constexpr bool own = OWN;
+    const int band_lin = static_cast<int>(blockIdx.x) * B + (wave >> lw);
+    const int n_out = own ? band_lin * kTileRows + 4 * (lane >> 4) + (lane & 3)
+                          : static_cast<int>(blockIdx.x) * B * kTileRows + tid;
     const uint32_t n_ws = static_cast<uint32_t>(min(n_out, N - 1));
     // unconditional: no branch, no early wait
     const uint16_t wsb = ws[(static_cast<uint64_t>(n_ws) * seg_mul) >> seg_shift];
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     // sinking them past the barrier to their use.
     double cs = 0.0;
     int offset = 0;
-    if (wave == 0) {
+    if (own || wave == 0) {
         cs = static_cast<double>(bf16_to_float(wsb)) * (1.0 / static_cast<double>(sm));
         for (int i = 0; i < W; ++i) offset -= 2 * xsum_sh[i];
         asm volatile("" : "+v"(cs), "+v"(offset));
@@ -193,7 +204,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = r.a1[i] + (r.a4[i] >> 2) + (r.a16[i] >> 4);   // exact
     // lane l now holds row 4*(l/16) + l%4 of its band (replicated over l/4 % 4)
-    part_sh[wave][lane] = row_group_reduce(v, lane);
+    const int rsum = row_group_reduce(v, lane);
+    if (own) {
+        if (((lane >> 2) & 3) == 0 && n_out < N) {
+            const int total = rsum + offset;
+            y[n_out] = epilogue_bf16_scaled(total, cs, bf16_to_float(wsb), sm);
+            if (acc) acc[n_out] = total;
+        }
+        return;
+    }
+    part_sh[wave][lane] = rsum;
     __syncthreads();
 
     // 4. Wavefront 0, lane l < 16*B: row l % 16 of band l / 16 -- add the
@@ -344,14 +364,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_local_kernel(
     }
 }
 
-constexpr int kMaxSteps = 20;
+// K <= kGemvMaxK = 61440 is at most 240 steps, which 16 wavefronts per band
+// take in runs of at most 15.
+constexpr int kMaxSteps = 15;
 
 using GemvFn = void (*)(const void*, const v4u*, const float*, const uint16_t*, uint32_t, int,
                         uint16_t*, int32_t*, int8_t*, float*, int, int, int, int);
 
-template <bool FUSED, int C, int... Ps>
+template <bool FUSED, int C, bool OWN, int... Ps>
 constexpr std::array<GemvFn, sizeof...(Ps)> kernel_table(std::integer_sequence<int, Ps...>) {
-    return {{&gemv_kernel<Ps + 1, FUSED, C>...}};
+    return {{&gemv_kernel<Ps + 1, FUSED, C, OWN>...}};
 }
 
 template <int... Ps>
@@ -367,12 +389,18 @@ const std::array<GemvFn, kLocalMaxSteps> kLocalKernels =
     local_table(std::make_integer_sequence<int, kLocalMaxSteps>{});
 // [fused][log2 C][P - 1]
 const std::array<std::array<KernelRow, 3>, 2> kKernels = {{
-    {{kernel_table<false, 1>(std::make_integer_sequence<int, kMaxSteps>{}),
-      kernel_table<false, 2>(std::make_integer_sequence<int, kMaxSteps>{}),
-      kernel_table<false, 4>(std::make_integer_sequence<int, kMaxSteps>{})}},
-    {{kernel_table<true, 1>(std::make_integer_sequence<int, kMaxSteps>{}),
-      kernel_table<true, 2>(std::make_integer_sequence<int, kMaxSteps>{}),
-      kernel_table<true, 4>(std::make_integer_sequence<int, kMaxSteps>{})}},
+    {{kernel_table<false, 1, false>(std::make_integer_sequence<int, kMaxSteps>{}),
+      kernel_table<false, 2, false>(std::make_integer_sequence<int, kMaxSteps>{}),
+      kernel_table<false, 4, false>(std::make_integer_sequence<int, kMaxSteps>{})}},
+    {{kernel_table<true, 1, false>(std::make_integer_sequence<int, kMaxSteps>{}),
+      kernel_table<true, 2, false>(std::make_integer_sequence<int, kMaxSteps>{}),
+      kernel_table<true, 4, false>(std::make_integer_sequence<int, kMaxSteps>{})}},
+}};
+// int8 input with one wavefront per band: [log2 C][P - 1]
+const std::array<KernelRow, 3> kKernelsOwn = {{
+    kernel_table<false, 1, true>(std::make_integer_sequence<int, kMaxSteps>{}),
+    kernel_table<false, 2, true>(std::make_integer_sequence<int, kMaxSteps>{}),
+    kernel_table<false, 4, true>(std::make_integer_sequence<int, kMaxSteps>{}),
 }};
 
 hipError_t launch(bool fused, const void* x, const uint8_t* packed, const float* s,
@@ -391,7 +419,8 @@ hipError_t launch(bool fused, const void* x, const uint8_t* packed, const float*
     const int threads = g.waves * 64;
     const int need = (chunks + threads - 1) / threads;
     const int lc = need <= 1 ? 0 : need <= 2 ? 1 : 2;
-    GemvFn fn = kKernels[fused ? 1 : 0][lc][g.steps - 1];
+    GemvFn fn = (!fused && wb == 1) ? kKernelsOwn[lc][g.steps - 1]
+                                    : kKernels[fused ? 1 : 0][lc][g.steps - 1];
     size_t lds_bytes = lds;
     // the wave-local bf16 kernel where it measured faster (see its comment)
     if (fused && g.bands == 1 && g.waves <= 4 && groups <= 256 && g.steps <= kLocalMaxSteps) {

@@ -53,8 +53,11 @@ def prefill_asm(tmp_path_factory):
 
 
 def test_weight_loads_issued_before_first_wait(gemv_asm):
-    kernels = list(re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])ELi(\d)E\S*):", gemv_asm, re.M))
-    assert len(kernels) == 120   # P = 1..20, int8 and bf16 input, C = 1, 2, 4 cached chunks
+    kernels = list(re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])ELi(\d)ELb([01])E\S*):", gemv_asm,
+                               re.M))
+    # P = 1..15, int8 and bf16 input, C = 1, 2, 4 cached chunks; int8 also with
+    # one wavefront per band finishing its own rows
+    assert len(kernels) == 135
     late = []
     for m in kernels:
         P = int(m.group(2))
@@ -112,12 +115,14 @@ def test_no_scratch_and_declared_lds_only(gemv_asm, mfma_asm):
     # No kernel spills to scratch, and each uses exactly the LDS it declares:
     # a private array that the compiler moves into LDS (it does so for arrays
     # indexed at run time) once made the MFMA kernel twice as slow.
-    for m in re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])ELi(\d)E\S*):", gemv_asm, re.M):
-        name, fused = m.group(1), m.group(3) == "1"
+    for m in re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])ELi(\d)ELb([01])E\S*):", gemv_asm,
+                         re.M):
+        name, fused, own = m.group(1), m.group(3) == "1", m.group(5) == "1"
         assert _meta(gemv_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
-        # part_sh[16][64] + xsum_sh[16], + amax_sh[16] when fused (the
-        # activation row itself is dynamic LDS)
-        want = 16 * 64 * 4 + 16 * 4 + (16 * 4 if fused else 0)
+        # part_sh[16][64] (not when each wavefront finishes its own rows) +
+        # xsum_sh[16], + amax_sh[16] when fused (the activation row itself is
+        # dynamic LDS)
+        want = (0 if own else 16 * 64 * 4) + 16 * 4 + (16 * 4 if fused else 0)
         assert _meta(gemv_asm, name, "amdhsa_group_segment_fixed_size") == want, name
     for m in re.finditer(r"^(_ZN\S*gemv_local_kernelILi(\d+)E\S*):", gemv_asm, re.M):
         name = m.group(1)
