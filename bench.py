@@ -157,7 +157,9 @@ def fused(bl, steps, warmup):
     return ms
 
 
-def layer_shapes(bl, steps, warmup):
+def layer_shapes(bl, steps, warmup, lut=False):
+    """The int8 layer set through bitlinear_i8xi2, or through the table-lookup GEMV
+    (bitlinear_lut_i8xi2, the cross-check algorithm) when lut is set."""
     torch = _torch()
     out = {}
     lib = bl.lib()
@@ -172,11 +174,17 @@ def layer_shapes(bl, steps, warmup):
         y = torch.empty((1, c.N), dtype=torch.bfloat16, device="cuda")
 
         def launch(i, c=c, xq=xq, s=s, ws=ws, y=y, ptrs=ptrs, n_copies=n_copies):
-            rc = lib.bitlinear_i8xi2(xq.data_ptr(), ptrs[i % n_copies], s.data_ptr(),
-                                     ws.data_ptr(), c.ws_num, y.data_ptr(), None, 1, c.N, c.K,
-                                     torch.cuda.current_stream().cuda_stream)
+            st = torch.cuda.current_stream().cuda_stream
+            if lut:
+                rc = lib.bitlinear_lut_i8xi2(xq.data_ptr(), ptrs[i % n_copies], s.data_ptr(),
+                                             ws.data_ptr(), c.ws_num, y.data_ptr(), None, c.N,
+                                             c.K, st)
+            else:
+                rc = lib.bitlinear_i8xi2(xq.data_ptr(), ptrs[i % n_copies], s.data_ptr(),
+                                         ws.data_ptr(), c.ws_num, y.data_ptr(), None, 1, c.N, c.K,
+                                         st)
             if rc != 0:
-                raise RuntimeError(f"bitlinear_i8xi2 failed: {rc}")
+                raise RuntimeError(f"layer launch failed: {rc}")
 
         ms = time_graph(launch, steps, warmup)
         b = gemv_bytes(1, c.N, c.K, c.ws_num)
@@ -436,7 +444,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only")
     ap.add_argument("--sections",
-                    default="fused,layer_set,batched,prefill,decode_step,chained_step,ternarize,torch",
+                    default="fused,layer_set,lut,batched,prefill,decode_step,chained_step,ternarize,torch",
                     help="detail sections to run after the headline (comma list; for profiling one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -478,6 +486,8 @@ def main():
                                            "GBps": round(fb / (fms * 1e-3) / 1e9, 1)}
     if "layer_set" in sections:
         detail["layer_set_int8"] = layer_shapes(bl, max(args.steps // 4, 100), 50)
+    if "lut" in sections:
+        detail["layer_set_int8_lut"] = layer_shapes(bl, max(args.steps // 4, 100), 50, lut=True)
     if "batched" in sections:
         detail["batched_mfma"] = batched(bl, max(args.steps // 8, 50), 20)
     if "prefill" in sections:

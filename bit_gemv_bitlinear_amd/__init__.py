@@ -23,6 +23,7 @@ TERNARIZE_WORKSPACE_BYTES = 2048   # BL_TERNARIZE_WORKSPACE_BYTES
 GEMV_MAX_K = 61440
 # Largest K of the projection with its glue (bitlinear_rmsnorm_i8xi2).
 NORM_MAX_K = 32768
+LUT_MAX_K = 8192
 RMS_EPS = 1e-5
 
 # Entry points declared in include/bitlinear.h: name -> (restype, argtypes).
@@ -38,6 +39,7 @@ SIGNATURES = {
     "quantize_act_absmax_i8": (_I, [_P, _I, _P, _P, _I, _I, _P]),
     "bitlinear_i8xi2": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _P]),
     "bitlinear_bf16_i8xi2": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "bitlinear_lut_i8xi2": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _P]),
     "bitlinear_rmsnorm_i8xi2": (_I, [_P, _P, _P, ctypes.c_float, _P, _P, _I, _P, _P, _P, _P, _P,
                                      _P, _I, _I, _P]),
     "bl_graph_create": (_I, [_P, _I, ctypes.POINTER(_P)]),
@@ -200,6 +202,30 @@ def bitlinear_i8xi2(xq, packed, s, ws, N, ws_num=None, y=None, acc=None):
         _require(acc, torch.int32, "acc")
     _check(lib().bitlinear_i8xi2(_ptr(xq2), _ptr(packed), _ptr(s), _ptr(ws), ws_num, _ptr(y),
                                  _ptr(acc), M, N, K, _stream()), "bitlinear_i8xi2")
+    return y
+
+
+def bitlinear_lut_i8xi2(xq, packed, s, ws, N, ws_num=None, y=None, acc=None):
+    """The M = 1 layer by table lookup: int8 xq (K), packed weights, fp32 s (1), bf16 ws ->
+    bf16 y (N); the same bits as bitlinear_i8xi2 (a second algorithm, K <= LUT_MAX_K)."""
+    import torch
+    _require(xq, torch.int8, "xq")
+    _require(packed, torch.uint8, "packed")
+    _require(s, torch.float32, "s")
+    _require(ws, torch.bfloat16, "ws")
+    K = xq.shape[-1]
+    if xq.numel() != K or s.numel() != 1:
+        raise ValueError("bitlinear_lut_i8xi2 takes one activation row")
+    ws_num = ws.numel() if ws_num is None else ws_num
+    if packed.numel() != bl_packed_bytes(N, K):
+        raise ValueError("packed has the wrong size for (N, K)")
+    if y is None:
+        y = torch.empty((N,), dtype=torch.bfloat16, device=xq.device)
+    _require(y, torch.bfloat16, "y")
+    if acc is not None:
+        _require(acc, torch.int32, "acc")
+    _check(lib().bitlinear_lut_i8xi2(_ptr(xq), _ptr(packed), _ptr(s), _ptr(ws), ws_num, _ptr(y),
+                                     _ptr(acc), N, K, _stream()), "bitlinear_lut_i8xi2")
     return y
 
 

@@ -16,8 +16,8 @@ LIB = os.path.join(HERE, "libbitlinear.so")
 # measurement aid for bench.py (not part of the layer): its own library
 PROBE_SRC = os.path.join(HERE, "probe", "stream_floor.hip")
 PROBE_LIB = os.path.join(HERE, "libstream_floor.so")
-SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "gemv_norm.hip", "gemm_mfma.hip",
-           "gemm_prefill.hip", "ternarize.hip"]
+SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "gemv_norm.hip", "gemv_lut.hip",
+           "gemm_mfma.hip", "gemm_prefill.hip", "ternarize.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

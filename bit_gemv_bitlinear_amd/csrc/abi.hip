@@ -228,6 +228,16 @@ int bitlinear_bf16_i8xi2(const uint16_t* x, const uint8_t* packed, const uint16_
     return run_layer_bf16(x, packed, ws, ws_num, y, q_out, s_out, acc, M, N, K, stream);
 }
 
+int bitlinear_lut_i8xi2(const int8_t* xq, const uint8_t* packed, const float* s,
+                        const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int N, int K,
+                        hipStream_t stream) {
+    const int rc = check_layer_i8(xq, packed, s, ws, ws_num, y, acc, 1, N, K);
+    if (rc) return rc;
+    if (K > bl::kLutMaxK) return BL_ERR_SHAPE;
+    (void)hipGetLastError();
+    return status_of(bl::launch_gemv_lut(xq, packed, s, ws, ws_num, y, acc, N, K, stream));
+}
+
 int bitlinear_rmsnorm_i8xi2(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma,
                             float eps, const uint8_t* packed, const uint16_t* ws, int ws_num,
                             const uint16_t* residual, uint16_t* y, uint16_t* xn_out,

@@ -33,6 +33,7 @@ struct GemvShape {
 };
 constexpr int kGemvMaxK = 61440;   // LDS copy of the row <= 60 KiB
 constexpr int kNormMaxK = 32768;   // the projection with its glue (launch_gemv_norm)
+constexpr int kLutMaxK = 8192;     // the table-lookup GEMV: tables of the row in LDS (K * 17 B)
 GemvShape gemv_shape(int N, int K);
 
 // M == 1, int8 activations; K <= kGemvMaxK.
@@ -44,6 +45,12 @@ hipError_t launch_gemv_i8(const int8_t* xq, const uint8_t* packed, const float* 
 hipError_t launch_gemv_bf16_fused(const uint16_t* x, const uint8_t* packed, const uint16_t* ws,
                                   int ws_num, uint16_t* y, int8_t* q_out, float* s_out,
                                   int32_t* acc, int N, int K, hipStream_t stream);
+
+// M == 1, int8 activations, by table lookup (a cross-check of the dot-product
+// GEMV); K <= kLutMaxK.
+hipError_t launch_gemv_lut(const int8_t* xq, const uint8_t* packed, const float* s,
+                           const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int N, int K,
+                           hipStream_t stream);
 
 // M == 1 projection with its glue: [relu2-GLU of (x, x_up)] -> RMSNorm(gamma,
 // eps) -> per-token int8 quantisation -> ternary layer -> [+ residual];

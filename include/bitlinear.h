@@ -204,6 +204,25 @@ int bitlinear_bf16_i8xi2(const uint16_t* x, const uint8_t* packed, const uint16_
                          int M, int N, int K, hipStream_t stream);
 
 /*
+ * bitlinear_lut_i8xi2 -- the M = 1 layer on int8 activations by table lookup,
+ * a second algorithm for the same result as bitlinear_i8xi2 (same arguments
+ * with M = 1; the same acc and y bits).  After the LUT kernels of the CPU
+ * page "BitNet на микроконтроллерах: как устроен запуск 1.58-битной LLM на
+ * кластере ESP32-S3" (sarnas.ru; its sections on the LUT compilation of the
+ * weights and on the qgemm_lut kernel): every pair of activations (elements
+ * e and e + 4 of a 16-wide K chunk, e in 0..3 and 8..11) gets a table of its
+ * 16 sums (c0 - 2) x0 + (c1 - 2) x1 over 2-bit codes c0, c1, and each 4-bit
+ * nibble of a packed word -- the codes of such a pair -- selects one entry.
+ * The tables of the whole row live in LDS (17 K bytes).  It is a cross-check
+ * of the dot-product kernel, not a faster path on this GPU.
+ *   16 <= K <= 8192, K % 16 == 0; other arguments as bitlinear_i8xi2.
+ * Errors: as bitlinear_i8xi2 (BL_ERR_SHAPE for K > 8192).
+ */
+int bitlinear_lut_i8xi2(const int8_t* xq, const uint8_t* packed, const float* s,
+                        const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int N, int K,
+                        hipStream_t stream);
+
+/*
  * bitlinear_rmsnorm_i8xi2 -- one projection of a decode step with the glue
  * that joins it to the previous one.  [W2A8] §4.1 names the converted
  * model's norms (attention_norm and ffn_norm before the attention and MLP

@@ -101,6 +101,23 @@ def test_bitlinear_i8xi2_errors():
     assert _i8(y=U) == bl.BL_ERR_ALIGN
 
 
+def _lut(xq=A, packed=A, s=A, ws=A, ws_num=1, y=A, acc=None, N=64, K=256):
+    return bl.lib().bitlinear_lut_i8xi2(xq, packed, s, ws, ws_num, y, acc, N, K, None)
+
+
+def test_bitlinear_lut_errors():
+    assert _lut(xq=None) == bl.BL_ERR_NULL
+    assert _lut(packed=None) == bl.BL_ERR_NULL
+    assert _lut(s=None) == bl.BL_ERR_NULL
+    assert _lut(y=None) == bl.BL_ERR_NULL
+    assert _lut(N=0) == bl.BL_ERR_SHAPE
+    assert _lut(K=72) == bl.BL_ERR_SHAPE
+    assert _lut(K=bl.LUT_MAX_K + 16) == bl.BL_ERR_SHAPE     # the tables of the row in LDS
+    assert _lut(ws_num=3, N=64) == bl.BL_ERR_ARG
+    assert _lut(xq=U) == bl.BL_ERR_ALIGN
+    assert _lut(acc=A + 2) == bl.BL_ERR_ALIGN
+
+
 def test_bitlinear_bf16_errors():
     assert _bf(x=None) == bl.BL_ERR_NULL
     assert _bf(M=2) == bl.BL_ERR_NULL                    # M > 1 needs the staging buffers

@@ -175,3 +175,25 @@ def test_norm_kernels_issue_all_loads_first(norm_asm):
             late.append((P, C, glu, weights, rows))
         assert _meta(norm_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
     assert not late, f"(P, C, glu, weight loads, row loads before the first wait): {late}"
+
+
+@pytest.fixture(scope="module")
+def lut_asm(tmp_path_factory):
+    return _asm(tmp_path_factory, "gemv_lut.hip")
+
+
+def test_lut_kernels_issue_all_loads_first(lut_asm):
+    # gemv_lut_kernel<P>: all P weight tiles (after the activation chunks it
+    # builds tables from) are issued before the first wait, without scratch
+    kernels = list(re.finditer(r"^(_ZN\S*gemv_lut_kernelILi(\d+)E\S*):", lut_asm, re.M))
+    assert sorted(int(m.group(2)) for m in kernels) == list(range(1, 33))   # K <= 8192
+    late = []
+    for m in kernels:
+        name, P = m.group(1), int(m.group(2))
+        body = lut_asm[m.end():lut_asm.index("s_endpgm", m.end())]
+        first_wait = body.index("s_waitcnt vmcnt")
+        weights = len(re.findall(r"global_load_dwordx4 [^\n]* nt\b", body[:first_wait]))
+        if weights != P:
+            late.append((P, weights))
+        assert _meta(lut_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
+    assert not late, f"(P, weight loads before the first wait): {late}"
