@@ -97,9 +97,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     // 4 * (l / 16) + l % 4, where the row reduction leaves that row's sum.
     // Otherwise wavefront 0 writes row tid of the workgroup's bands after a
     // barrier.  Measured same-box at 13824 x 2560 with int8 input: 3.60 ->
-    // 3.54 us; with bf16 input every wavefront's ws / s, formed after the
-    // quantisation, lengthens the path to the main loop (3.65 -> 3.76 us),
-    // so the fused kernels keep the barrier.
+    // 3.41 us.  With bf16 input every wavefront forms ws / s after the
+    // quantisation, on its path to the main loop, and the gain shrinks to
+    // 3.65 -> 3.62 us: not worth 45 more kernels, so only the int8 kernels
+    // are compiled with OWN.
     constexpr bool own = OWN;
     const int band_lin = static_cast<int>(blockIdx.x) * B + (wave >> lw);
     const int n_out = own ? band_lin * kTileRows + 4 * (lane >> 4) + (lane & 3)
