@@ -24,7 +24,8 @@ namespace {
 // The glue runs in the prologue of every workgroup (the row is at most a few
 // thousand elements, read from L2 by each): no kernel of its own, so a chained
 // decode step launches one kernel per projection.  Everything else is the
-// staged kernel above: the weight loads are all issued before the first wait.
+// staged GEMV of gemv.hip (its pieces in gemv_core.hpp): the weight loads are
+// all issued before the first wait.
 // ---------------------------------------------------------------------------
 
 // Sum of a double over the 64 lanes: the two 32-bit halves move together
