@@ -73,11 +73,13 @@ def test_model_projection_with_glue(bl, proj):
                    residual=h)
 
 
-# (6400, 2320) and (16, 28688): rows longer than the chunks a thread caches,
-# so the kernel's loop over uncached chunks runs
+# (6400, 2320), (16, 28688) and (64, 32768): rows longer than the chunks a
+# thread caches, so the kernel's loop over uncached chunks runs; K = 32768 is
+# the largest, 16 steps per wavefront
 @pytest.mark.parametrize("N,K,ws_num,glu", [(100, 272, 2, False), (16, 16, 1, True),
                                             (1000, 4096, 4, True), (8200, 512, 1, False),
-                                            (6400, 2320, 2, True), (16, 28688, 1, False)])
+                                            (6400, 2320, 2, True), (16, 28688, 1, False),
+                                            (64, 32768, 2, True)])
 def test_ragged_shapes(bl, N, K, ws_num, glu):
     g = synth.rng(N + K)
     x = synth.normal_bf16_bits(g, 1, K).reshape(-1)

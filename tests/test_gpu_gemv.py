@@ -68,8 +68,10 @@ def test_large_set_with_device_quantiser(bl, idx):
     check_i8(bl, c.name, c.w, qo, so, c.ws, c.ws_num)
 
 
+# (33, 61440): the GEMV's largest K (16 wavefronts per band, 15 steps each);
+# (20, 61456): one step past it, which M = 1 takes through the MFMA kernel
 RAGGED = [(1, 16), (64, 16), (65, 80), (100, 208), (64 * 3 + 7, 64 * 5 + 48), (4097, 1040),
-          (127, 6912 + 16), (640, 13824)]
+          (127, 6912 + 16), (640, 13824), (33, 61440), (20, 61456)]
 
 
 @pytest.mark.parametrize("N,K", RAGGED)
@@ -126,7 +128,7 @@ def test_output_buffer_fully_written(bl):
 
 FUSED = [("qkv", 3840, 2560, 1), ("o", 2560, 2560, 1), ("gate_up", 13824, 2560, 2),
          ("down", 2560, 6912, 1), ("ragged", 100, 208, 1), ("k13824", 5120, 13824, 1),
-         ("tiny", 1, 16, 1)]
+         ("tiny", 1, 16, 1), ("kmax", 48, 61440, 1)]
 
 
 @pytest.mark.parametrize("name,N,K,ws_num", FUSED)
