@@ -53,6 +53,16 @@ __device__ __forceinline__ uint16_t bf16_from_double_rne(double v) {
     return static_cast<uint16_t>(sign | static_cast<uint32_t>(bits));
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed bf16 (a in the low half), nearest with ties to
+// even: v_cvt_pk_bf16_f32 in the default rounding mode.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // The epilogue of [W2A8] §5.3 under the reading y = acc * ws / s: the
 // activation scale s = 127/amax multiplied x on the way in, so it divides
 // here.  The result is bf16_rne(fl64(acc * ws) / s) -- the product is exact,

@@ -24,9 +24,10 @@
 //     4 x MTW 16x16 int32 tiles in registers for all of K -- no reduction
 //     across wavefronts;
 //   * with the weights as the A operand, a lane's result is four
-//     consecutive output columns n of one row m: the epilogue rounds them
-//     in single precision (the exact division only next to a bf16 rounding
-//     midpoint) and stores 8 bytes.
+//     consecutive output columns n of one row m: the epilogue multiplies
+//     them in fp64 by ws / s, converts to fp32 and packs them to bf16 (the
+//     exact division only where an fp32 value is a bf16 midpoint), and
+//     stores 8 bytes.
 #include <algorithm>
 #include <array>
 
@@ -46,10 +47,6 @@ namespace {
 constexpr int kAPitch = 272;
 constexpr int kWRowGroupWords = 72;
 constexpr int kWTileWords = 4 * kWRowGroupWords;
-// Single-precision epilogue: margin (in units of the product's last bit)
-// around a bf16 rounding midpoint inside which the exact path is taken.
-constexpr uint32_t kNearMidpoint = 16;
-
 __device__ __forceinline__ v4i decode_w(uint32_t w) {
     v4i b;
     b.x = static_cast<int>(__builtin_amdgcn_perm(0u, kCodeToInt8, w & 0x03030303u));
@@ -59,21 +56,33 @@ __device__ __forceinline__ v4i decode_w(uint32_t w) {
     return b;
 }
 
-// The bf16 value of acc * ws / s (the exact path's: the fp64 quotient
-// rounded to bf16) from c = fl32(ws * fl32(1 / s)).  p = fl32(fl32(acc) * c)
-// carries at most four roundings of 2^-24 (relative), so it lies within 4
-// units of its last bit of the quotient; with ws and 1/s in [2^-50, 2^45]
-// (checked by the caller) p is normal or zero.  Unless p's low 16 bits lie
-// within kNearMidpoint units of the bf16 midpoint 0x8000, no rounding
-// boundary separates p from the quotient and p's rounding is the answer.
-__device__ __forceinline__ bool bf16_from_c32(int32_t acc, float c, uint32_t& out) {
-    const uint32_t b = __float_as_uint(static_cast<float>(acc) * c);
-    out = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-    return ((b & 0xFFFFu) - (0x8000u - kNearMidpoint)) > 2u * kNearMidpoint;
-}
-
-__device__ __forceinline__ bool scale_in_range(float v) {
-    return v >= 0x1p-50f && v <= 0x1p45f;
+// y = bf16(fl64(acc * ws) / s), the §5.3 epilogue, for a group of four
+// outputs, without a division on the common path.  v = fl64(acc * cs) with
+// cs = fl64(ws * fl64(1 / s)) lies within 2^-51 (relative) of the quotient.
+// It goes to bf16 through fp32 (one conversion to fp32, then
+// v_cvt_pk_bf16_f32): every bf16 midpoint is an fp32 number, and a midpoint
+// lying between v and the quotient, or one the fp64 quotient rounds onto, is
+// so close to v that v's nearest fp32 is that midpoint -- among fp32
+// subnormals too, which keep 16 more bits than bf16's.  So the two
+// roundings give the exact path's bf16 unless the fp32 value is a midpoint
+// (low 16 bits 0x8000), about one output in 65536; a group holding one is
+// redone exactly, by the whole wavefront in one uniform branch.
+__device__ __forceinline__ uint2 epilogue4(const int (&acc)[4], const float (&ws)[4],
+                                           const double (&cs)[4], float s) {
+    float f[4];
+    uint64_t redo = 0;   // lanes with a midpoint, one ballot per compare
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        f[v] = static_cast<float>(static_cast<double>(acc[v]) * cs[v]);
+        redo |= __builtin_amdgcn_ballot_w64((__float_as_uint(f[v]) & 0xFFFFu) == 0x8000u);
+    }
+    uint2 o{cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3])};
+    if (__builtin_expect(redo != 0, 0)) {
+        asm volatile("");   // kept a branch: if-converted it would cost every group its divisions
+        o.x = epilogue_bf16(acc[0], ws[0], s) | (static_cast<uint32_t>(epilogue_bf16(acc[1], ws[1], s)) << 16);
+        o.y = epilogue_bf16(acc[2], ws[2], s) | (static_cast<uint32_t>(epilogue_bf16(acc[3], ws[3], s)) << 16);
+    }
+    return o;
 }
 
 // WN x WMW wavefronts; wavefront tile 64 weight rows x 16 * MTW activation rows.
@@ -223,39 +232,38 @@ __global__ __launch_bounds__(WN * WMW * 64) void gemm_prefill_kernel(
     // Epilogue.  D layout with the weights as the A operand: lane (j, g),
     // register v -> weight row 4g + v of the band, activation row j of the
     // m tile: four consecutive outputs of one row, one 8-byte store.
-    bool scales_ok = true;
+    double wsd[4][4];
 #pragma unroll
     for (int tw = 0; tw < 4; ++tw)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) scales_ok = scales_ok && scale_in_range(wsf[tw][v]);
-    float rs[MTW];
-#pragma unroll
-    for (int mt = 0; mt < MTW; ++mt) {
-        rs[mt] = 1.0f / sm[mt];
-        scales_ok = scales_ok && scale_in_range(rs[mt]);
-    }
+        for (int v = 0; v < 4; ++v) wsd[tw][v] = static_cast<double>(wsf[tw][v]);
+    // 8-byte stores wherever four outputs fit: every group of a row when N is
+    // a multiple of 4 and y is 8-byte aligned
+    const bool y_vec = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) {
         const int m = m_base + 16 * (MTW * wm + mt) + j;
+        const double rs = 1.0 / static_cast<double>(sm[mt]);
 #pragma unroll
         for (int tw = 0; tw < 4; ++tw) {
             const int n = n_base + 64 * wn + 16 * tw + 4 * g;
-            if (m >= M || n >= N) continue;
             const int acc[4] = {c[tw][mt].x, c[tw][mt].y, c[tw][mt].z, c[tw][mt].w};
-            uint32_t o[4];
+            double cs[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const bool fast = scales_ok && bf16_from_c32(acc[v], wsf[tw][v] * rs[mt], o[v]);
-                if (!fast) o[v] = epilogue_bf16(acc[v], wsf[tw][v], sm[mt]);
-            }
+            for (int v = 0; v < 4; ++v) cs[v] = wsd[tw][v] * rs;
+            // every lane takes part (the exact branch is wave-uniform); only
+            // rows and columns inside the layer are stored
+            const uint2 o = epilogue4(acc, wsf[tw], cs, sm[mt]);
+            if (m >= M || n >= N) continue;
             const size_t off = static_cast<size_t>(m) * N + n;
             uint16_t* yo = y + off;
-            if (n + 4 <= N && (reinterpret_cast<uintptr_t>(yo) & 7) == 0) {
-                *reinterpret_cast<uint2*>(yo) = uint2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+            if (y_vec && n + 4 <= N) {
+                *reinterpret_cast<uint2*>(yo) = o;
             } else {
+                const uint32_t ov[4] = {o.x & 0xFFFFu, o.x >> 16, o.y & 0xFFFFu, o.y >> 16};
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    if (n + v < N) yo[v] = static_cast<uint16_t>(o[v]);
+                    if (n + v < N) yo[v] = static_cast<uint16_t>(ov[v]);
             }
             if (acc_out) {
                 int32_t* ao = acc_out + off;

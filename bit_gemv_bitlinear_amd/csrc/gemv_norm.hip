@@ -93,16 +93,6 @@ __device__ __forceinline__ uint32_t bf16_rne_f64(double d) {
     return d != d ? 0x7FC0u : u;
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two fp32 values to packed bf16 (a in the low half), nearest with ties to
-// even: v_cvt_pk_bf16_f32 in the default rounding mode.
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-    const f32x2_t v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
 // Eight fp64 values to bf16 (nearest, ties to even) by way of fp32: one
 // conversion to fp32, one to bf16.  Every bf16 midpoint is an fp32 number,
 // so the first rounding can land on one but never step across one: the two
@@ -111,19 +101,19 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 // again by bf16_rne_f64.
 __device__ __forceinline__ uint4 bf16x8_from_f64(const double (&d)[8]) {
     uint32_t o[4];
-    bool redo = false;
+    uint64_t redo = 0;   // lanes that need it, one ballot per compare
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const float f0 = static_cast<float>(d[2 * j]), f1 = static_cast<float>(d[2 * j + 1]);
-        redo = redo | ((__float_as_uint(f0) & 0xFFFFu) == 0x8000u);
-        redo = redo | ((__float_as_uint(f1) & 0xFFFFu) == 0x8000u);
-        redo = redo | __builtin_isunordered(f0, f1);
+        redo |= __builtin_amdgcn_ballot_w64((__float_as_uint(f0) & 0xFFFFu) == 0x8000u);
+        redo |= __builtin_amdgcn_ballot_w64((__float_as_uint(f1) & 0xFFFFu) == 0x8000u);
+        redo |= __builtin_amdgcn_ballot_w64(__builtin_isunordered(f0, f1));
         o[j] = cvt_pk_bf16(f0, f1);
     }
     // a wave-uniform branch, taken by a wavefront when any of its lanes needs
     // it (rarely); the empty volatile statement keeps the compiler from
     // if-converting it, which would pay its work on every chunk
-    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+    if (__builtin_expect(redo != 0, 0)) {
         asm volatile("");
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = bf16_rne_f64(d[2 * j]) | (bf16_rne_f64(d[2 * j + 1]) << 16);

@@ -7,8 +7,9 @@ down after relu(gate)^2 * up and ffn_sub_norm plus the residual -- compared outp
 output: the normalised row, its int8 quantisation and scale, the int32 accumulators and
 the bf16 result.  Then rows that are not multiples of the kernel's tiles, the smallest K,
 a zero row, a large-magnitude row, eps = 0, and a two-layer chain replayed as one graph.
-The normalised row is defined in fp64; the kernel's sum of squares runs in another order,
-so the bar is 1 ulp, but on these seeded inputs every value is expected to match exactly.
+The normalised row is defined in fp64; the kernel adds the squares in another order, which
+could in principle move a value by 1 ulp, but no input here does: every output is asserted
+exactly equal.
 """
 import numpy as np
 import pytest

@@ -8,9 +8,8 @@ the oracle on every row and the layer on sampled rows (each output row
 depends only on its own activation row, so the rows the oracle computes
 one by one are exact references for the full-size launch).  Smaller
 shapes compare every output: M, N and K not multiples of the kernel's
-tiles, weight-scale segments that split bands, activation scales outside
-the single-precision epilogue's range (its exact path), and the bf16
-entry point.  int32 accumulators must match exactly; bf16 outputs too
+tiles, weight-scale segments that split bands, activation scales from
+1e-30 to 3e20, and the bf16 entry point.  int32 accumulators must match exactly; bf16 outputs too
 (the bar is 1 ulp; the kernel rounds the exact quotient).
 """
 import numpy as np
@@ -85,8 +84,9 @@ def test_prefill_segments_and_extremes(bl):
     xq[1] = 127
     xq[2] = 0
     s = synth.act_scale(g, M)
-    # activation scales whose reciprocal falls outside [2^-50, 2^45]: the
-    # epilogue's exact path for those rows
+    # activation scales far from 1 (their reciprocals beyond 2^45 and below
+    # 2^-50): the epilogue's fp64 product and its rounding through fp32 must
+    # hold there too
     s[3] = np.float32(1e-30)
     s[4] = np.float32(3e20)
     s[5] = np.float32(2.5e-14)
