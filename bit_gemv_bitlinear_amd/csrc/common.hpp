@@ -113,6 +113,35 @@ __device__ __forceinline__ uint16_t epilogue_bf16_scaled(int32_t acc, double cs,
     return out;
 }
 
+// y = bf16(fl64(acc * ws) / s), the §5.3 epilogue, for a group of four
+// outputs, without a division on the common path.  v = fl64(acc * cs) with
+// cs = fl64(ws * fl64(1 / s)) lies within 2^-51 (relative) of the quotient.
+// It goes to bf16 through fp32 (one conversion to fp32, then
+// v_cvt_pk_bf16_f32): every bf16 midpoint is an fp32 number, and a midpoint
+// lying between v and the quotient, or one the fp64 quotient rounds onto, is
+// so close to v that v's nearest fp32 is that midpoint -- among fp32
+// subnormals too, which keep 16 more bits than bf16's.  So the two
+// roundings give the exact path's bf16 unless the fp32 value is a midpoint
+// (low 16 bits 0x8000), about one output in 65536; a group holding one is
+// redone exactly, by the whole wavefront in one uniform branch.
+__device__ __forceinline__ uint2 epilogue4(const int (&acc)[4], const float (&ws)[4],
+                                           const double (&cs)[4], float s) {
+    float f[4];
+    uint64_t redo = 0;   // lanes with a midpoint, one ballot per compare
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        f[v] = static_cast<float>(static_cast<double>(acc[v]) * cs[v]);
+        redo |= __builtin_amdgcn_ballot_w64((__float_as_uint(f[v]) & 0xFFFFu) == 0x8000u);
+    }
+    uint2 o{cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3])};
+    if (__builtin_expect(redo != 0, 0)) {
+        asm volatile("");   // kept a branch: if-converted it would cost every group its divisions
+        o.x = epilogue_bf16(acc[0], ws[0], s) | (static_cast<uint32_t>(epilogue_bf16(acc[1], ws[1], s)) << 16);
+        o.y = epilogue_bf16(acc[2], ws[2], s) | (static_cast<uint32_t>(epilogue_bf16(acc[3], ws[3], s)) << 16);
+    }
+    return o;
+}
+
 // Per-activation quantisation of [W2A8] §六 item 3: q = clamp(round half
 // to even of fl32(x * s), -128, 127), for finite x and s = 127 / amax with
 // |x| <= amax.  Then |fl32(x * s)| <= 127 * (1 + 2^-24)^2 < 127.5, so the

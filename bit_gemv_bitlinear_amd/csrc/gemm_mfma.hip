@@ -27,8 +27,9 @@
 //     loads issued together hide their latency (PS * MT <= 20 bounds the
 //     registers);
 //   * the wavefronts' int32 tiles are added with LDS atomics (exact in any
-//     order), then the epilogue writes bf16 through the division-free fp64
-//     rounding (and optionally int32).
+//     order), then the epilogue writes bf16 four outputs at a time through
+//     epilogue4 (fp64 product, fp32, packed bf16; the division only where
+//     an fp32 value is a bf16 midpoint), and optionally int32.
 #include <algorithm>
 #include <array>
 #include <utility>
@@ -216,22 +217,26 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
     float wsf[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) wsf[e] = bf16_to_float(wsb[e]);
+    // (MT * 256 and the block size are multiples of 64, so every lane of a
+    // wavefront makes the same trips: epilogue4's branch stays uniform)
     for (int i = tid; i < MT * 16 * 16; i += nthreads) {
         const int ml = i >> 4;
         const int m = m0 + ml;
+        const int4 t = *reinterpret_cast<const int4*>(&red[ml][c4]);
+        const double inv = inv_s_sh[ml];
+        const float sm = s_sh[ml];
+        const int tv[4] = {t.x, t.y, t.z, t.w};
+        double cs[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[e] = static_cast<double>(wsf[e]) * inv;
+        const uint2 ob = epilogue4(tv, wsf, cs, sm);
+        const uint32_t o0 = ob.x & 0xFFFFu, o1 = ob.x >> 16, o2 = ob.y & 0xFFFFu, o3 = ob.y >> 16;
         if (m < M && n0 < N) {
-            const int4 t = *reinterpret_cast<const int4*>(&red[ml][c4]);
-            const double inv = inv_s_sh[ml];
-            const float sm = s_sh[ml];
-            const uint32_t o0 = epilogue_bf16_scaled(t.x, static_cast<double>(wsf[0]) * inv, wsf[0], sm);
-            const uint32_t o1 = epilogue_bf16_scaled(t.y, static_cast<double>(wsf[1]) * inv, wsf[1], sm);
-            const uint32_t o2 = epilogue_bf16_scaled(t.z, static_cast<double>(wsf[2]) * inv, wsf[2], sm);
-            const uint32_t o3 = epilogue_bf16_scaled(t.w, static_cast<double>(wsf[3]) * inv, wsf[3], sm);
             const size_t o = static_cast<size_t>(m) * N + n0;
             uint16_t* yo = y + o;
             const bool full = n0 + 4 <= N;
             if (full && (reinterpret_cast<uintptr_t>(yo) & 7) == 0) {
-                *reinterpret_cast<uint2*>(yo) = uint2{o0 | (o1 << 16), o2 | (o3 << 16)};
+                *reinterpret_cast<uint2*>(yo) = ob;
             } else {
                 yo[0] = static_cast<uint16_t>(o0);
                 if (n0 + 1 < N) yo[1] = static_cast<uint16_t>(o1);
