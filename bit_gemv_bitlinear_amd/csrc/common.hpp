@@ -72,44 +72,26 @@ __device__ __forceinline__ uint16_t epilogue_bf16(int32_t acc, float ws, float s
     return bf16_from_double_rne(v);
 }
 
-// bf16 rounding of an fp64 value in bf16's normal range, on the two 32-bit
-// halves of its encoding: the 7 kept fraction bits are bits 13..19 of the
-// high word, the round bit is bit 12, the sticky bits are the rest.  Returns
-// false -- leaving the value to the general path -- outside the normal range
-// (zero excepted) and when the value lies within 64 units of its last bit of
-// a rounding boundary.
-__device__ __forceinline__ bool bf16_rne_fast(double v, uint16_t& out) {
-    const uint32_t hi = static_cast<uint32_t>(__double2hiint(v));
-    const uint32_t lo = static_cast<uint32_t>(__double2loint(v));
-    const uint32_t sign = (hi >> 16) & 0x8000u;
-    const uint32_t exp = (hi >> 20) & 0x7FFu;
-    const uint32_t low13 = hi & 0x1FFFu;
-    const uint32_t mant7 = (hi >> 13) & 0x7Fu;
-    const uint32_t round = (hi >> 12) & 1u;
-    const uint32_t sticky = ((hi & 0xFFFu) | lo) != 0u;
-    const uint32_t up = round & (sticky | (mant7 & 1u));
-    // carries into the exponent when the fraction overflows (to inf from the
-    // top binade, as round-to-nearest requires)
-    const uint32_t bits = ((exp - 896u) << 7) + mant7 + up;
-    const bool zero = ((hi & 0x7FFFFFFFu) | lo) == 0u;
-    const bool normal = (exp >= 897u) && (exp <= 1150u);
-    const bool near = (low13 == 0x1000u && lo <= 64u) || (low13 == 0x0FFFu && lo >= 0xFFFFFFC0u);
-    out = static_cast<uint16_t>(sign | (zero ? 0u : bits));
-    return zero || (normal && !near);
-}
-
 // The same value as epilogue_bf16 without a division on the common path.
-// cs = fl64(ws * fl64(1/s)) is formed once per kernel; acc * cs, rounded to
-// fp64, carries four roundings and lies within 2^-50 (relative) of the fp64
-// quotient, i.e. within 8 units of its last bit.  Its bf16 rounding is
-// therefore the quotient's unless it sits within 64 units of a rounding
-// boundary (or outside bf16's normal range), in which case the quotient
-// itself is computed and rounded.
+// cs = fl64(ws * fl64(1/s)) is formed once per kernel; v = fl64(acc * cs)
+// carries three roundings and lies within 2^-51 (relative) of the quotient.
+// v goes to bf16 through fp32 (one conversion, then v_cvt_pk_bf16_f32):
+// every bf16 midpoint is an fp32 number, and a midpoint lying between v and
+// the quotient, or one the fp64 quotient rounds onto, is so close to v that
+// v's nearest fp32 is that midpoint -- among fp32 subnormals too, which keep
+// 16 more bits than bf16's.  So the two roundings give the exact path's
+// value unless the fp32 value is a midpoint (low 16 bits 0x8000, about one
+// output in 65536) or NaN; then every active lane of the wavefront takes the
+// exact path, in one uniform branch.
 __device__ __forceinline__ uint16_t epilogue_bf16_scaled(int32_t acc, double cs, float ws,
                                                          float s) {
-    uint16_t out;
-    if (!bf16_rne_fast(static_cast<double>(acc) * cs, out))
+    const float f = static_cast<float>(static_cast<double>(acc) * cs);
+    uint16_t out = static_cast<uint16_t>(cvt_pk_bf16(f, 0.0f));
+    const bool redo = ((__float_as_uint(f) & 0xFFFFu) == 0x8000u) || __builtin_isnan(f);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(redo) != 0, 0)) {
+        asm volatile("");   // kept a branch: if-converted it would cost every output its division
         out = epilogue_bf16(acc, ws, s);
+    }
     return out;
 }
 
@@ -122,8 +104,8 @@ __device__ __forceinline__ uint16_t epilogue_bf16_scaled(int32_t acc, double cs,
 // so close to v that v's nearest fp32 is that midpoint -- among fp32
 // subnormals too, which keep 16 more bits than bf16's.  So the two
 // roundings give the exact path's bf16 unless the fp32 value is a midpoint
-// (low 16 bits 0x8000), about one output in 65536; a group holding one is
-// redone exactly, by the whole wavefront in one uniform branch.
+// (low 16 bits 0x8000), about one output in 65536, or NaN; a group holding
+// one is redone exactly, by the whole wavefront in one uniform branch.
 __device__ __forceinline__ uint2 epilogue4(const int (&acc)[4], const float (&ws)[4],
                                            const double (&cs)[4], float s) {
     float f[4];
@@ -133,6 +115,8 @@ __device__ __forceinline__ uint2 epilogue4(const int (&acc)[4], const float (&ws
         f[v] = static_cast<float>(static_cast<double>(acc[v]) * cs[v]);
         redo |= __builtin_amdgcn_ballot_w64((__float_as_uint(f[v]) & 0xFFFFu) == 0x8000u);
     }
+    redo |= __builtin_amdgcn_ballot_w64(__builtin_isunordered(f[0], f[1]) ||
+                                        __builtin_isunordered(f[2], f[3]));
     uint2 o{cvt_pk_bf16(f[0], f[1]), cvt_pk_bf16(f[2], f[3])};
     if (__builtin_expect(redo != 0, 0)) {
         asm volatile("");   // kept a branch: if-converted it would cost every group its divisions
