@@ -22,7 +22,8 @@
 //     v_mfma_i32_16x16x64_i8 A operand, reads MTW activation operands
 //     (lane (j, g): row m = j, chunk g) as the B operand, and accumulates
 //     4 x MTW 16x16 int32 tiles in registers for all of K -- no reduction
-//     across wavefronts;
+//     across wavefronts; the A operand is the unsigned codes w + 2, and the
+//     epilogue takes 2 * sum(x) of each activation row off its outputs;
 //   * with the weights as the A operand, a lane's result is four
 //     consecutive output columns n of one row m: the epilogue multiplies
 //     them in fp64 by ws / s, converts to fp32 and packs them to bf16 (the
@@ -47,12 +48,15 @@ namespace {
 constexpr int kAPitch = 272;
 constexpr int kWRowGroupWords = 72;
 constexpr int kWTileWords = 4 * kWRowGroupWords;
+// The unsigned codes c = w + 2 of one packed word as the MFMA's A operand,
+// K order restored by shifting each 2-bit field down (padding stays 0): the
+// MFMA then sums c * x, and the epilogue takes 2 * sum(x) off each row.
 __device__ __forceinline__ v4i decode_w(uint32_t w) {
     v4i b;
-    b.x = static_cast<int>(__builtin_amdgcn_perm(0u, kCodeToInt8, w & 0x03030303u));
-    b.y = static_cast<int>(__builtin_amdgcn_perm(0u, kCodeToInt8, (w >> 2) & 0x03030303u));
-    b.z = static_cast<int>(__builtin_amdgcn_perm(0u, kCodeToInt8, (w >> 4) & 0x03030303u));
-    b.w = static_cast<int>(__builtin_amdgcn_perm(0u, kCodeToInt8, (w >> 6) & 0x03030303u));
+    b.x = static_cast<int>(w & 0x03030303u);
+    b.y = static_cast<int>((w >> 2) & 0x03030303u);
+    b.z = static_cast<int>((w >> 4) & 0x03030303u);
+    b.w = static_cast<int>((w >> 6) & 0x03030303u);
     return b;
 }
 
@@ -142,6 +146,11 @@ __global__ __launch_bounds__(WN * WMW * 64) void gemm_prefill_kernel(
     // second set, loading two tiles ahead, measured no faster).
     v4i ra[kAChunks];
     v4u rw[kWTiles];
+    // sum of this thread's activation bytes per chunk row, over real K only
+    // (a chunk past K re-reads the last one and must not count)
+    int xsum[kAChunks];
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) xsum[i] = 0;
     auto load_tile = [&](int kt) {
         const uint32_t kc = min(kt * kTileK + a_col, K - 16);
 #pragma unroll
@@ -153,10 +162,15 @@ __global__ __launch_bounds__(WN * WMW * 64) void gemm_prefill_kernel(
         for (int i = 0; i < kWTiles; ++i)
             rw[i] = __builtin_nontemporal_load(w_src[i] + static_cast<size_t>(kt) * 64);
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, int kt) {
+        const bool real = kt * kTileK + a_col < K;
 #pragma unroll
-        for (int i = 0; i < kAChunks; ++i)
+        for (int i = 0; i < kAChunks; ++i) {
             *reinterpret_cast<v4i*>(&a_lds[buf][(r0 + (kThreads / 16) * i) * kAPitch + a_col]) = ra[i];
+            if (real)
+                xsum[i] = dot4(ra[i].x, 0x01010101, dot4(ra[i].y, 0x01010101,
+                               dot4(ra[i].z, 0x01010101, dot4(ra[i].w, 0x01010101, xsum[i]))));
+        }
 #pragma unroll
         for (int i = 0; i < kWTiles; ++i)
             if (w_has[i]) *reinterpret_cast<v4u*>(&w_lds[buf][w_dst[i]]) = rw[i];
@@ -191,14 +205,28 @@ __global__ __launch_bounds__(WN * WMW * 64) void gemm_prefill_kernel(
     };
 
     load_tile(0);
-    store_tile(0);
+    store_tile(0, 0);
     __syncthreads();
     for (int kt = 0; kt < S256; ++kt) {
         if (kt + 1 < S256) load_tile(kt + 1);
         compute_tile(kt & 1);
-        if (kt + 1 < S256) store_tile((kt + 1) & 1);
+        if (kt + 1 < S256) store_tile((kt + 1) & 1, kt + 1);
         __syncthreads();
     }
+    // 2 * sum(x) of each activation row: the 16 threads of a row (lanes
+    // 16q .. 16q + 15) add their sums with DPP inside the row of lanes; one
+    // writes it to the first row of the (now idle) activation buffer
+    int* twice_sum = reinterpret_cast<int*>(&a_lds[0][0]);
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) {
+        int v = xsum[i];
+        v += dpp_row<kDppQuadXor1>(v);
+        v += dpp_row<kDppQuadXor2>(v);
+        v += dpp_row<kDppRowRor4>(v);
+        v += dpp_row<kDppRowRor8>(v);
+        if ((tid & 15) == 0) twice_sum[r0 + (kThreads / 16) * i] = 2 * v;
+    }
+    __syncthreads();
 
     // Epilogue.  D layout with the weights as the A operand: lane (j, g),
     // register v -> weight row 4g + v of the band, activation row j of the
@@ -218,7 +246,9 @@ __global__ __launch_bounds__(WN * WMW * 64) void gemm_prefill_kernel(
 #pragma unroll
         for (int tw = 0; tw < 4; ++tw) {
             const int n = n_base + 64 * wn + 16 * tw + 4 * g;
-            const int acc[4] = {c[tw][mt].x, c[tw][mt].y, c[tw][mt].z, c[tw][mt].w};
+            const int off2 = twice_sum[16 * (MTW * wm + mt) + j];
+            const int acc[4] = {c[tw][mt].x - off2, c[tw][mt].y - off2, c[tw][mt].z - off2,
+                                c[tw][mt].w - off2};
             double cs[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) cs[v] = wsd[tw][v] * rs;
