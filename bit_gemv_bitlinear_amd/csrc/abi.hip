@@ -65,11 +65,14 @@ int check_layer_bf16(const uint16_t* x, const uint8_t* packed, const uint16_t* w
 }
 
 // The LDS-tiled kernel (both operands reused across a workgroup) beats the
-// one that streams the weights per 64-row chunk from 128 activation rows on
-// for wide layers (13824 x 2560: 17.1 against 18.5 us at M = 128, 32 against
-// 55 us at M = 512); for narrow ones (N <= 3840) it measured no faster or
-// slower, too few of its larger tiles to fill the chip.
-constexpr int kPrefillMinM = 128;
+// one that streams the weights per 64-row chunk as soon as that one needs a
+// second chunk, M > 64, for wide layers (13824 x 2560, same box: 13.6 against
+// 16.0 us at M = 65, 13.5 against 16.4 at M = 96, 28 against 55 at M = 512);
+// up to M = 64 it is slower (12.7 against 10.1 us at M = 64), and for narrow
+// layers (N <= 3840) it is slower at every M measured (11.8 against 9.2 us at
+// 3840 x 2560, 24.2 against 16.3 at 2560 x 6912, M = 96), too few of its
+// larger tiles to fill the chip.
+constexpr int kPrefillMinM = 65;
 constexpr int kPrefillMinN = 8192;
 
 int check_norm(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma, float eps,

@@ -172,7 +172,7 @@ int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int 
  * The activation scale divides: s = 127/amax quantised the activations, so
  * y approximates x . w^T * ws.
  * M == 1 with K <= 61440 runs the GEMV kernel (workgroups of 1, 2 or 4
- * 16-row bands, v_dot4 on masked codes).  M >= 128 with N >= 8192 (prompt
+ * 16-row bands, v_dot4 on masked codes).  M >= 65 with N >= 8192 (prompt
  * processing on wide layers, the prompt lengths of [W2A8] §7.2) runs the
  * LDS-tiled int8 MFMA kernel (v_mfma_i32_16x16x64_i8; workgroup tiles of up
  * to 256 weight rows x 128 activation rows reuse both operands); any other

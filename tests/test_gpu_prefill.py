@@ -65,7 +65,8 @@ def test_prefill_gate_up(bl, M):
     check_rows(acc, y, c.w, qo, so, c.ws, c.ws_num, rows)
 
 
-@pytest.mark.parametrize("M,N,K", [(130, 8240, 528), (257, 8192, 272), (128, 8256, 2560)])
+@pytest.mark.parametrize("M,N,K", [(130, 8240, 528), (257, 8192, 272), (128, 8256, 2560), (65, 8256, 528),
+                                   (100, 13824, 1024)])
 def test_prefill_ragged(bl, M, N, K):
     c = synth.make_int8_gemv(f"p{M}", M, N, K, 1, synth.seed_for(9, 0, M + K))
     print(f"prefill ragged M={M} N={N} K={K}", flush=True)
