@@ -41,8 +41,10 @@ PEAK_INT8_TOPS = 5000.0          # MI355X dense int8 MFMA, published peak (TOP/s
 A100_W2A8_GBS_13824x2560 = 473.5  # the page's 18.75 us on A100 (§7.1), as GB/s by the same formula
 CACHE_DEFEAT_BYTES = 512 << 20
 PROFILE_PMC = os.path.join(ROOT, "profiles", "gemv_i8_13824x2560_pmc.txt")
+# the headline kernel's sources and the build script that holds its compile flags
 GEMV_SOURCES = [os.path.join(ROOT, "bit_gemv_bitlinear_amd", "csrc", f)
-                for f in ("gemv.hip", "gemv_core.hpp", "common.hpp")]
+                for f in ("gemv.hip", "gemv_core.hpp", "common.hpp")] + \
+               [os.path.join(ROOT, "bit_gemv_bitlinear_amd", "build.py")]
 PROBE_LIB = os.path.join(ROOT, "bit_gemv_bitlinear_amd", "libstream_floor.so")
 
 

@@ -46,6 +46,15 @@ hipError_t launch_gemv_bf16_fused(const uint16_t* x, const uint8_t* packed, cons
                                   int ws_num, uint16_t* y, int8_t* q_out, float* s_out,
                                   int32_t* acc, int N, int K, hipStream_t stream);
 
+// The wave-local variant of the bf16 GEMV: one band per workgroup, `waves`
+// (<= 4) wavefronts of `steps` (<= kLocalMaxSteps) K steps, 2^lw = waves;
+// seg_mul / seg_shift from seg_divisor(N / ws_num).
+constexpr int kLocalMaxSteps = 12;
+hipError_t launch_gemv_local(const uint16_t* x, const uint8_t* packed, const uint16_t* ws,
+                             uint32_t seg_mul, int seg_shift, uint16_t* y, int32_t* acc,
+                             int8_t* q_out, float* s_out, int N, int K, unsigned groups,
+                             int waves, int steps, int lw, hipStream_t stream);
+
 // M == 1, int8 activations, by table lookup (a cross-check of the dot-product
 // GEMV); K <= kLutMaxK.
 hipError_t launch_gemv_lut(const int8_t* xq, const uint8_t* packed, const float* s,

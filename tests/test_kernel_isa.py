@@ -25,7 +25,7 @@ def _asm(tmp_path_factory, source):
     if not os.path.exists(build.HIPCC):
         pytest.skip("hipcc not available")
     out = tmp_path_factory.mktemp("isa") / source.replace(".hip", ".s")
-    flags = [f for f in build.FLAGS if f != "-fPIC"]
+    flags = [f for f in build.flags_for(source) if f != "-fPIC"]
     cmd = [build.HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, source),
            "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
@@ -35,6 +35,11 @@ def _asm(tmp_path_factory, source):
 @pytest.fixture(scope="module")
 def gemv_asm(tmp_path_factory):
     return _asm(tmp_path_factory, "gemv.hip")
+
+
+@pytest.fixture(scope="module")
+def local_asm(tmp_path_factory):
+    return _asm(tmp_path_factory, "gemv_local.hip")
 
 
 @pytest.fixture(scope="module")
@@ -69,13 +74,33 @@ def test_weight_loads_issued_before_first_wait(gemv_asm):
     assert not late, f"(P, fused, weight loads before the first wait): {late}"
 
 
-def test_local_weight_loads_issued_before_first_wait(gemv_asm):
-    kernels = list(re.finditer(r"^(_ZN\S*gemv_local_kernelILi(\d+)E\S*):", gemv_asm, re.M))
+def test_gemv_arguments_preloaded(gemv_asm):
+    # gemv.hip is built with its kernels' first 14 argument dwords preloaded
+    # into SGPRs: after the compatibility prologue (which loads them the usual
+    # way and jumps over 256 bytes), no kernel-argument load may come before
+    # the weight loads have been issued
+    kernels = list(re.finditer(r"^(_ZN\S*gemv_kernelILi(\d+)ELb([01])ELi(\d)ELb([01])E\S*):", gemv_asm,
+                               re.M))
+    assert len(kernels) == 135
+    late = []
+    for m in kernels:
+        name = m.group(1)
+        assert _meta(gemv_asm, name, "amdhsa_user_sgpr_kernarg_preload_length") == 14, name
+        body = gemv_asm[m.end():gemv_asm.index("s_endpgm", m.end())]
+        main = body[body.index("s_branch"):]
+        first_wait = main.index("s_waitcnt vmcnt")
+        if "s_load_" in main[:first_wait]:
+            late.append(name)
+    assert not late, f"kernel-argument loads ahead of the weight loads: {late}"
+
+
+def test_local_weight_loads_issued_before_first_wait(local_asm):
+    kernels = list(re.finditer(r"^(_ZN\S*gemv_local_kernelILi(\d+)E\S*):", local_asm, re.M))
     assert sorted(int(m.group(2)) for m in kernels) == list(range(1, 13))
     late = []
     for m in kernels:
         P = int(m.group(2))
-        body = gemv_asm[m.end():gemv_asm.index("s_endpgm", m.end())]
+        body = local_asm[m.end():local_asm.index("s_endpgm", m.end())]
         first_wait = body.index("s_waitcnt vmcnt")
         weights = len(re.findall(r"global_load_dwordx4 [^\n]* nt\b", body[:first_wait]))
         acts = len(re.findall(r"global_load_dwordx2 ", body[:first_wait]))
@@ -111,7 +136,7 @@ def _meta(asm, name, key):
     return int(re.search(r"\." + key + r"\s+(\d+)", block).group(1))
 
 
-def test_no_scratch_and_declared_lds_only(gemv_asm, mfma_asm):
+def test_no_scratch_and_declared_lds_only(gemv_asm, local_asm, mfma_asm):
     # No kernel spills to scratch, and each uses exactly the LDS it declares:
     # a private array that the compiler moves into LDS (it does so for arrays
     # indexed at run time) once made the MFMA kernel twice as slow.
@@ -124,11 +149,11 @@ def test_no_scratch_and_declared_lds_only(gemv_asm, mfma_asm):
         # dynamic LDS)
         want = (0 if own else 16 * 64 * 4) + 16 * 4 + (16 * 4 if fused else 0)
         assert _meta(gemv_asm, name, "amdhsa_group_segment_fixed_size") == want, name
-    for m in re.finditer(r"^(_ZN\S*gemv_local_kernelILi(\d+)E\S*):", gemv_asm, re.M):
+    for m in re.finditer(r"^(_ZN\S*gemv_local_kernelILi(\d+)E\S*):", local_asm, re.M):
         name = m.group(1)
-        assert _meta(gemv_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
+        assert _meta(local_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
         # part_sh[16][64] + amax_sh[16] (the quantised words are dynamic LDS)
-        assert _meta(gemv_asm, name, "amdhsa_group_segment_fixed_size") == 16 * 64 * 4 + 16 * 4, name
+        assert _meta(local_asm, name, "amdhsa_group_segment_fixed_size") == 16 * 64 * 4 + 16 * 4, name
     for m in re.finditer(r"^(_ZN\S*gemm_mfma_kernelILi(\d+)ELi(\d+)E\S*):", mfma_asm, re.M):
         name, MT = m.group(1), int(m.group(2))
         assert _meta(mfma_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
