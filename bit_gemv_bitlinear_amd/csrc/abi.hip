@@ -18,14 +18,19 @@ namespace {
 
 constexpr int kMaxK = 1 << 20;
 constexpr int kMaxN = 1 << 24;
+// Rows of activations: the MFMA kernels' grids (N/64 x M/64 workgroups, or
+// one dimension of at most M*N/2^15 workgroups of 512 threads) stay far
+// inside the launch limits, as does the quantiser's one workgroup per row.
+constexpr int kMaxM = 1 << 20;
+constexpr long long kMaxOutputs = 1LL << 36;   // M * N
 constexpr int kMaxWsNum = 64;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int check_mnk(int M, int N, int K) {
-    if (M < 1 || N < 1 || K < 16 || (K % 16) != 0 || K > kMaxK || N > kMaxN) return BL_ERR_SHAPE;
-    // the largest output buffer indexed with size_t; M * N bounded for int grids
-    if (static_cast<long long>(M) * N > (1LL << 40)) return BL_ERR_SHAPE;
+    if (M < 1 || N < 1 || K < 16 || (K % 16) != 0 || K > kMaxK || N > kMaxN || M > kMaxM)
+        return BL_ERR_SHAPE;
+    if (static_cast<long long>(M) * N > kMaxOutputs) return BL_ERR_SHAPE;
     return BL_OK;
 }
 
@@ -207,7 +212,7 @@ int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int 
                            hipStream_t stream) {
     if (!x || !q || !s) return BL_ERR_NULL;
     if (x_dtype != 0 && x_dtype != 1) return BL_ERR_ARG;
-    if (M < 1 || K < 16 || (K % 16) != 0 || K > kMaxK) return BL_ERR_SHAPE;
+    if (M < 1 || M > kMaxM || K < 16 || (K % 16) != 0 || K > kMaxK) return BL_ERR_SHAPE;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return BL_ERR_ALIGN;
     (void)hipGetLastError();
     return status_of(bl::launch_quant(x, x_dtype, q, s, M, K, stream));

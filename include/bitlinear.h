@@ -33,8 +33,8 @@
  *     outputs do not overlap.
  *   - Alignment: xq, x, packed and q_out 16 bytes; s, s_out, acc 4 bytes;
  *     ws, y 2 bytes.  Otherwise BL_ERR_ALIGN.
- *   - Shapes: M >= 1, N >= 1, K >= 16 with K % 16 == 0, K <= 1048576,
- *     N <= 16777216.  Otherwise BL_ERR_SHAPE.
+ *   - Shapes: 1 <= M <= 1048576, N >= 1, K >= 16 with K % 16 == 0,
+ *     K <= 1048576, N <= 16777216, M * N <= 2^36.  Otherwise BL_ERR_SHAPE.
  *   - Activation inputs must be finite; scales must be finite and > 0.
  *     These are not checked on the device; other values give undefined
  *     results (never out-of-bounds accesses).

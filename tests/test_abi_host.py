@@ -91,6 +91,10 @@ def test_bitlinear_i8xi2_errors():
     assert _i8(K=8) == bl.BL_ERR_SHAPE
     assert _i8(K=72) == bl.BL_ERR_SHAPE                  # K % 16 != 0
     assert _i8(K=(1 << 20) + 16) == bl.BL_ERR_SHAPE
+    assert _i8(N=(1 << 24) + 16) == bl.BL_ERR_SHAPE
+    assert _i8(M=(1 << 20) + 1) == bl.BL_ERR_SHAPE
+    assert _i8(M=1 << 20, N=(1 << 16) + 16) == bl.BL_ERR_SHAPE   # M * N > 2^36
+    assert _bf(M=(1 << 20) + 1) == bl.BL_ERR_SHAPE
     assert _i8(ws_num=0) == bl.BL_ERR_ARG
     assert _i8(ws_num=3, N=64) == bl.BL_ERR_ARG          # N % ws_num != 0
     assert _i8(ws_num=65, N=65 * 64) == bl.BL_ERR_ARG
@@ -135,6 +139,7 @@ def test_quantize_and_pack_errors():
     assert q(A, 2, A, A, 1, 64, None) == bl.BL_ERR_ARG
     assert q(A, 0, A, A, 0, 64, None) == bl.BL_ERR_SHAPE
     assert q(A, 0, A, A, 1, 24, None) == bl.BL_ERR_SHAPE
+    assert q(A, 0, A, A, (1 << 20) + 1, 64, None) == bl.BL_ERR_SHAPE
     assert q(A + 4, 1, A, A, 1, 64, None) == bl.BL_ERR_ALIGN
     p = bl.lib().pack_ternary_weights
     assert p(None, A, 64, 64, None, None) == bl.BL_ERR_NULL
