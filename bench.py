@@ -396,10 +396,12 @@ def gemv_geometry(N, K):
     M=1 GEMV for this shape (the same rule as gemv_shape in bit_gemv_bitlinear_amd/csrc/gemv.hip)."""
     S = -(-K // 256)
     nbands = -(-N // 16)
-    target = 4 if nbands < 400 else 10
+    target = 4 if nbands < 400 else 5 if nbands < 768 else 10
     Wb = 1
     while Wb < 16 and -(-S // Wb) > target:
         Wb *= 2
+    while Wb > 8 and -(-S // (Wb // 2)) <= 15:
+        Wb //= 2
     P = -(-S // Wb)
     B = 4
     while B > 1 and (nbands // B < 200 or B * Wb > 16):

@@ -312,10 +312,14 @@ GemvShape gemv_shape(int N, int K) {
     const int S = (K + kTileK - 1) / kTileK;
     const int nbands = (N + kTileRows - 1) / kTileRows;
     // Wavefronts per band: the smallest power of two (the kernel splits by
-    // shifts) that leaves at most the target number of steps per wavefront.
-    const int target = nbands < kNarrowBands ? kTargetStepsNarrow : kTargetSteps;
+    // shifts) that leaves at most the target number of steps per wavefront,
+    // then no more than kBandWaves while the runs fit the kernels.
+    const int target = nbands < kNarrowBands ? kTargetStepsNarrow
+                       : nbands < kWideBands ? kTargetStepsMedium
+                                             : kTargetSteps;
     int Wb = 1;
     while (Wb < kMaxWaves && (S + Wb - 1) / Wb > target) Wb <<= 1;
+    while (Wb > kBandWaves && (S + Wb / 2 - 1) / (Wb / 2) <= kMaxSteps) Wb >>= 1;
     const int P = (S + Wb - 1) / Wb;
     if (P > kMaxSteps) return GemvShape{0, 0, 0};
     // Bands per workgroup: as many as keep >= kMinGroups workgroups in flight.

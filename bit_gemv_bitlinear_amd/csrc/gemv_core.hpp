@@ -100,5 +100,17 @@ constexpr int kMinGroups = 200;     // workgroups wanted in flight (256 CUs)
 constexpr int kTargetSteps = 10;
 constexpr int kTargetStepsNarrow = 4;
 constexpr int kNarrowBands = 400;
+// The M = 1 GEMV adds a middle tier and a cap (gemv_shape; a same-box sweep
+// of the wavefronts per band over 16 shapes, int8 and bf16 input).  Between
+// kNarrowBands and kWideBands bands, runs of at most 5: with one wavefront
+// per band too few are in flight (6912 x 2560: 3.00 -> 2.87 us int8, 3.64 ->
+// 3.13 us bf16).  And at most kBandWaves wavefronts per band while their
+// runs stay within the kernels' steps: a band's 16 wavefronts cost more in
+// their reduction than their shorter runs save (2560 x 13824: 4.77 -> 3.89
+// us int8, 5.80 -> 4.88 bf16; 3200 x 10240: 4.12 -> 3.46, 5.25 -> 3.86;
+// 5120 x 13824: 6.76 -> 6.06, 8.75 -> 7.73).
+constexpr int kTargetStepsMedium = 5;
+constexpr int kWideBands = 768;
+constexpr int kBandWaves = 8;
 
 }  // namespace bl
