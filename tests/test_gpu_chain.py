@@ -176,7 +176,14 @@ def test_chained_two_layers_as_graph(bl):
         r = oracle.chained_layer(L.w, L.ws, L.ws_num, L.gamma, L.attn_out, hb)
         want.append(r)
         hb = r["h2"]
-    for rep in range(3):   # replays with host synchronisation between them
+    scratch = torch.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        # every output poisoned, and unrelated eager work, between replays
+        for o in outs:
+            for k in ("qkv", "h1", "gu", "h2"):
+                o[k].fill_(float("nan"))
+        scratch.mul_(1.0001)
+        torch.cuda.synchronize()
         graph.launch()
         torch.cuda.synchronize()
         for l in range(n_layers):
