@@ -26,9 +26,13 @@
 //     per 16-K chunk, with packed 16-bit adds (8 per pair), chunk stride 272
 //     bytes so that the 16 chunks a wavefront reads at once start on
 //     different banks;
-//   * one wavefront per band of 16 rows, all its P = S weight tiles loaded
-//     up front; per K step a lane looks up 8 entries for each of its 4 rows;
-//     then the row reduction and epilogue of the dot-product kernel.
+//   * Wb wavefronts per band of 16 rows split its S K steps, P each (all
+//     loaded up front), B bands per workgroup sharing its tables; per K step
+//     a lane looks up 8 entries for each of its 4 rows; then the row
+//     reduction (across the Wb wavefronts through LDS) and the epilogue of
+//     the dot-product kernel.  The lookups are VALU work in proportion to
+//     the weights, so they are spread over many wavefronts (runs of at most
+//     kLutTargetSteps), unlike the dot-product kernel's runs of up to 10.
 // Bound: LDS lookups and VALU (8 lookups per packed word against 4 dot4 in
 // the dot-product kernel); the weights stream from HBM as there.
 #include <array>
@@ -43,7 +47,10 @@ namespace bl {
 namespace {
 
 constexpr int kLutChunkStride = 272;   // 8 pair tables x 32 bytes + 16 bytes of bank offset
-constexpr int kLutMaxX = 8;            // 16-byte activation chunks per thread (K / 16 <= 512)
+// 16-byte activation chunks a thread builds tables for: one, since every
+// wavefront takes at most 4 steps, so S <= 4 Wb and the S * 16 chunks are no
+// more than the band's 64 Wb threads (the launcher checks it).
+constexpr int kLutMaxX = 1;
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
@@ -101,26 +108,32 @@ __device__ __forceinline__ int lookup_word(const uint8_t* lut, int base, uint32_
     return acc;
 }
 
-// B bands per workgroup (one wavefront each), P = S K steps per wavefront.
+// B bands per workgroup, 2^lw wavefronts per band, P K steps per wavefront
+// (steps past the row's S are skipped).
+constexpr int kLutMaxWaves = 8;
 template <int P>
-__global__ __launch_bounds__(256) void gemv_lut_kernel(
+__global__ __launch_bounds__(kLutMaxWaves * 64) void gemv_lut_kernel(
     const int8_t* __restrict__ xq, const v4u* __restrict__ packed, const float* __restrict__ s_in,
     const uint16_t* __restrict__ ws, uint32_t seg_mul, int seg_shift, uint16_t* __restrict__ y,
-    int32_t* __restrict__ acc, int N, int K, int B) {
+    int32_t* __restrict__ acc, int N, int K, int B, int lw) {
     extern __shared__ uint4 lut_sh[];
+    __shared__ int part_sh[kLutMaxWaves][64];
     uint8_t* lut = reinterpret_cast<uint8_t*>(lut_sh);
-    const int nthreads = B * 64;
+    const int Wb = 1 << lw;
+    const int nthreads = (B << lw) * 64;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nbands = (N + kTileRows - 1) / kTileRows;
-    const int band_lin = static_cast<int>(blockIdx.x) * B + wave;
+    const int band_lin = static_cast<int>(blockIdx.x) * B + (wave >> lw);
     const int band = min(band_lin, nbands - 1);
-    const int chunks = P * 16;   // 16-K chunks of the padded row
+    const int S = (K + kTileK - 1) / kTileK;
+    const int s0 = (wave & (Wb - 1)) * P;
+    const int chunks = S * 16;   // 16-K chunks of the padded row
 
     // 1. This lane's output row and weight scale, the activation chunks this
     //    thread builds tables for (buffer loads: zeros past the row's end),
-    //    then every weight tile of the band.
+    //    then every weight tile of this wavefront's steps.
     const int n_out = band_lin * kTileRows + 4 * (lane >> 4) + (lane & 3);
     const uint32_t n_ws = static_cast<uint32_t>(min(n_out, N - 1));
     const uint16_t wsb = ws[(static_cast<uint64_t>(n_ws) * seg_mul) >> seg_shift];
@@ -132,9 +145,9 @@ __global__ __launch_bounds__(256) void gemv_lut_kernel(
 #pragma unroll
     for (int j = 0; j < kLutMaxX; ++j)
         if (j < nx) xv[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (tid + j * nthreads) * 16, 0, 0);
-    const v4u* tiles = packed + static_cast<size_t>(band) * P * 64 + lane;
+    const v4u* tiles = packed + static_cast<size_t>(band) * S * 64 + lane;
     v4u w[P];
-    load_steps<P>(tiles, 0, P - 1, w);
+    load_steps<P>(tiles, s0, S - 1, w);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
@@ -159,19 +172,29 @@ __global__ __launch_bounds__(256) void gemv_lut_kernel(
     const double cs = static_cast<double>(bf16_to_float(wsb)) * (1.0 / static_cast<double>(s));
     __syncthreads();
 
-    // 3. Lookups: step u, K chunk u * 16 + lane % 16, the four rows of the slot.
+    // 3. Lookups: step s0 + u, K chunk (s0 + u) * 16 + lane % 16, the four
+    //    rows of the slot; a step past the row's end is skipped (uniform).
     int v[4] = {0, 0, 0, 0};
     const int kc = lane & 15;
 #pragma unroll
     for (int u = 0; u < P; ++u) {
-        const int base = (u * 16 + kc) * kLutChunkStride;
-        v[0] = lookup_word(lut, base, w[u].x, v[0]);
-        v[1] = lookup_word(lut, base, w[u].y, v[1]);
-        v[2] = lookup_word(lut, base, w[u].z, v[2]);
-        v[3] = lookup_word(lut, base, w[u].w, v[3]);
+        if (s0 + u < S) {
+            const int base = ((s0 + u) * 16 + kc) * kLutChunkStride;
+            v[0] = lookup_word(lut, base, w[u].x, v[0]);
+            v[1] = lookup_word(lut, base, w[u].y, v[1]);
+            v[2] = lookup_word(lut, base, w[u].z, v[2]);
+            v[3] = lookup_word(lut, base, w[u].w, v[3]);
+        }
     }
-    // 4. Row reduction; lane l with (l / 4) % 4 == 0 writes row 4 (l / 16) + l % 4.
-    const int total = row_group_reduce(v, lane);
+    // 4. Row reduction (lane l with (l / 4) % 4 == 0 holds row 4 (l / 16) + l % 4),
+    //    then the band's first wavefront adds its Wb partial sums and writes.
+    int total = row_group_reduce(v, lane);
+    if (Wb > 1) {
+        part_sh[wave][lane] = total;
+        __syncthreads();
+        if ((wave & (Wb - 1)) != 0) return;
+        for (int j = 1; j < Wb; ++j) total += part_sh[wave + j][lane];
+    }
     if (((lane >> 2) & 3) == 0 && band_lin < nbands && n_out < N) {
         y[n_out] = epilogue_bf16_scaled(total, cs, bf16_to_float(wsb), s);
         if (acc) acc[n_out] = total;
@@ -179,14 +202,22 @@ __global__ __launch_bounds__(256) void gemv_lut_kernel(
 }
 
 using LutFn = void (*)(const int8_t*, const v4u*, const float*, const uint16_t*, uint32_t, int,
-                       uint16_t*, int32_t*, int, int, int);
+                       uint16_t*, int32_t*, int, int, int, int);
 
 template <int... Ps>
 constexpr std::array<LutFn, sizeof...(Ps)> lut_table(std::integer_sequence<int, Ps...>) {
     return {{&gemv_lut_kernel<Ps + 1>...}};
 }
 
-constexpr int kLutMaxSteps = kLutMaxK / kTileK;
+// K steps per wavefront aimed at: the smallest power of two of wavefronts
+// per band that leaves at most this many, then as many bands per workgroup
+// (at most kLutMaxWaves wavefronts in all) as keep kMinGroups workgroups.
+// K <= kLutMaxK is at most 32 steps: P <= 4 with 8 wavefronts.  Against one
+// wavefront per band (same box): 3840 x 2560 5.80 -> 3.50 us, 2560 x 6912
+// 11.88 -> 6.00, 6912 x 2560 5.52 -> 4.70, 20480 x 3200 12.11 -> 10.30, but
+// 13824 x 2560 6.30 -> 6.58 (16 wavefronts per workgroup there: 7.08).
+constexpr int kLutTargetSteps = 4;
+constexpr int kLutMaxSteps = kLutTargetSteps;
 const std::array<LutFn, kLutMaxSteps> kLutKernels =
     lut_table(std::make_integer_sequence<int, kLutMaxSteps>{});
 
@@ -198,25 +229,32 @@ hipError_t launch_gemv_lut(const int8_t* xq, const uint8_t* packed, const float*
     const int S = (K + kTileK - 1) / kTileK;
     if (K > kLutMaxK || S < 1) return hipErrorInvalidValue;
     const int nbands = (N + kTileRows - 1) / kTileRows;
+    int Wb = 1;
+    while (Wb < kLutMaxWaves && (S + Wb - 1) / Wb > kLutTargetSteps) Wb <<= 1;
+    const int P = (S + Wb - 1) / Wb;
+    if (P > kLutMaxSteps) return hipErrorInvalidValue;
+    int lw = 0;
+    while ((1 << lw) < Wb) ++lw;
     int B = 4;
-    while (B > 1 && nbands / B < kMinGroups) B >>= 1;
+    while (B > 1 && (nbands / B < kMinGroups || B * Wb > kLutMaxWaves)) B >>= 1;
+    if (S * 16 > B * Wb * 64 * kLutMaxX) return hipErrorInvalidValue;
     const unsigned groups = static_cast<unsigned>((nbands + B - 1) / B);
     const size_t lds = static_cast<size_t>(S) * 16 * kLutChunkStride;
     // Tables beyond 64 KiB (K > 3840) need the kernel's dynamic-LDS limit
-    // raised once.
+    // raised, once per kernel.
     static std::array<std::once_flag, kLutMaxSteps> raised;
     hipError_t attr = hipSuccess;
-    std::call_once(raised[S - 1], [&] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kLutKernels[S - 1]),
+    std::call_once(raised[P - 1], [&] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kLutKernels[P - 1]),
                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   static_cast<int>(kLutMaxSteps * 16 * kLutChunkStride));
+                                   static_cast<int>(kLutMaxK / kTileK * 16 * kLutChunkStride));
     });
     if (attr != hipSuccess) return attr;
     uint32_t seg_mul;
     int seg_shift;
     seg_divisor(N / ws_num, seg_mul, seg_shift);
-    kLutKernels[S - 1]<<<groups, B * 64, lds, stream>>>(
-        xq, reinterpret_cast<const v4u*>(packed), s, ws, seg_mul, seg_shift, y, acc, N, K, B);
+    kLutKernels[P - 1]<<<groups, B * Wb * 64, lds, stream>>>(
+        xq, reinterpret_cast<const v4u*>(packed), s, ws, seg_mul, seg_shift, y, acc, N, K, B, lw);
     return hipGetLastError();
 }
 
