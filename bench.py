@@ -535,7 +535,7 @@ def main():
                                "uniform ternary weights, uniform int8 activations, ws_num=2",
                    "M": 1, "N": c.N, "K": c.K, "ws_num": c.ws_num,
                    "bytes_per_gemv": nbytes, "weight_copies": n_copies,
-                   "timing": "one HIP graph of `steps` launches, HIP events on its stream"},
+                   "timing": "one HIP graph of `steps` launches after one untimed replay of it, HIP events on its stream"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
