@@ -47,9 +47,11 @@ namespace bl {
 namespace {
 
 constexpr int kLutChunkStride = 272;   // 8 pair tables x 32 bytes + 16 bytes of bank offset
-// 16-byte activation chunks a thread builds tables for: one, since every
+// 16-byte activation chunks a thread builds tables for: one.  Either every
 // wavefront takes at most 4 steps, so S <= 4 Wb and the S * 16 chunks are no
-// more than the band's 64 Wb threads (the launcher checks it).
+// more than the band's 64 Wb threads; or the matrix is wide (at least
+// 4 kMinGroups bands: 4 bands per workgroup, 256 threads) with at most
+// kLutWideSteps steps (160 chunks).  The launcher checks it.
 constexpr int kLutMaxX = 1;
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
@@ -217,7 +219,12 @@ constexpr std::array<LutFn, sizeof...(Ps)> lut_table(std::integer_sequence<int, 
 // 11.88 -> 6.00, 6912 x 2560 5.52 -> 4.70, 20480 x 3200 12.11 -> 10.30, but
 // 13824 x 2560 6.30 -> 6.58 (16 wavefronts per workgroup there: 7.08).
 constexpr int kLutTargetSteps = 4;
-constexpr int kLutMaxSteps = kLutTargetSteps;
+// Wide matrices (at least 4 kMinGroups bands, already about one wavefront
+// per SIMD) with rows of at most kLutWideSteps steps keep one wavefront per
+// band: 13824 x 2560 6.59 -> 6.00 us, 12816 x 2320 6.47 -> 5.96; at
+// 20480 x 3200 (13 steps) the split wins.
+constexpr int kLutWideSteps = 10;
+constexpr int kLutMaxSteps = kLutWideSteps;
 const std::array<LutFn, kLutMaxSteps> kLutKernels =
     lut_table(std::make_integer_sequence<int, kLutMaxSteps>{});
 
@@ -230,7 +237,8 @@ hipError_t launch_gemv_lut(const int8_t* xq, const uint8_t* packed, const float*
     if (K > kLutMaxK || S < 1) return hipErrorInvalidValue;
     const int nbands = (N + kTileRows - 1) / kTileRows;
     int Wb = 1;
-    while (Wb < kLutMaxWaves && (S + Wb - 1) / Wb > kLutTargetSteps) Wb <<= 1;
+    if (nbands < 4 * kMinGroups || S > kLutWideSteps)
+        while (Wb < kLutMaxWaves && (S + Wb - 1) / Wb > kLutTargetSteps) Wb <<= 1;
     const int P = (S + Wb - 1) / Wb;
     if (P > kLutMaxSteps) return hipErrorInvalidValue;
     int lw = 0;

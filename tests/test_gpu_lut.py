@@ -53,8 +53,10 @@ def test_lut_layer_set(bl, idx):
     check_lut(bl, c.name, c.w, c.xq, c.s, c.ws, c.ws_num)
 
 
+# (12816, 2320): a wide matrix (801 bands) with a ragged row of 10 steps, one
+# wavefront per band; the others split each band's steps over wavefronts
 @pytest.mark.parametrize("N,K,ws_num", [(100, 272, 2), (1, 16, 1), (17, 8192, 1), (3000, 4096, 4),
-                                        (8200, 512, 1), (64, 8176, 2)])
+                                        (8200, 512, 1), (64, 8176, 2), (12816, 2320, 2)])
 def test_lut_ragged(bl, N, K, ws_num):
     c = synth.make_int8_gemv(f"lut{N}x{K}", 1, N, K, ws_num, synth.seed_for(10, 0, N + K))
     check_lut(bl, c.name, c.w, c.xq, c.s, c.ws, c.ws_num)
