@@ -70,8 +70,11 @@ def test_large_set_with_device_quantiser(bl, idx):
 
 # (33, 61440): the GEMV's largest K (16 wavefronts per band, 15 steps each);
 # (20, 61456): one step past it, which M = 1 takes through the MFMA kernel
+# (6912, 2560): 432 bands, runs of 5 over two wavefronts per band; (3200, 10240)
+# and (2570, 13808): narrow with long rows, at most eight wavefronts per band
 RAGGED = [(1, 16), (64, 16), (65, 80), (100, 208), (64 * 3 + 7, 64 * 5 + 48), (4097, 1040),
-          (127, 6912 + 16), (640, 13824), (33, 61440), (20, 61456)]
+          (127, 6912 + 16), (640, 13824), (33, 61440), (20, 61456), (6912, 2560), (3200, 10240),
+          (2570, 13808)]
 
 
 @pytest.mark.parametrize("N,K", RAGGED)
