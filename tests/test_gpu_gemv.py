@@ -131,7 +131,8 @@ def test_output_buffer_fully_written(bl):
 
 FUSED = [("qkv", 3840, 2560, 1), ("o", 2560, 2560, 1), ("gate_up", 13824, 2560, 2),
          ("down", 2560, 6912, 1), ("ragged", 100, 208, 1), ("k13824", 5120, 13824, 1),
-         ("tiny", 1, 16, 1), ("kmax", 48, 61440, 1)]
+         ("tiny", 1, 16, 1), ("kmax", 48, 61440, 1), ("medium", 6912, 2560, 1),
+         ("narrow_long", 3200, 10240, 1)]
 
 
 @pytest.mark.parametrize("name,N,K,ws_num", FUSED)
