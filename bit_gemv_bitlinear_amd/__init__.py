@@ -46,6 +46,7 @@ SIGNATURES = {
     "bl_graph_create_norm": (_I, [_P, _I, ctypes.POINTER(_P)]),
     "bl_graph_launch": (_I, [_P, _P]),
     "bl_graph_size": (_I, [_P]),
+    "bl_graph_kernels": (_I, [_P]),
     "bl_graph_destroy": (_I, [_P]),
 }
 
@@ -103,13 +104,42 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _require(t, dtype, name):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+def _require(t, dtype, name, numel=None):
+    """Check a tensor argument before anything reaches the library: its dtype, that it is
+    contiguous and its element count when the call fixes one (an undersized buffer would be
+    read or written past its end by the kernel).  Every entry point checks all of its
+    tensors this way first, then that they live on the device (_on_device)."""
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the call needs {numel}")
+
+
+def _on_device(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
+def _optional(t, dtype, name, numel):
+    if t is not None:
+        _require(t, dtype, name, numel)
+
+
+def _ws_num(ws, ws_num):
+    """ws_num defaults to every scale of ws; an explicit one must lie within ws."""
+    if ws_num is None:
+        return ws.numel()
+    if not 1 <= ws_num <= ws.numel():
+        raise ValueError(f"ws_num = {ws_num} outside 1..{ws.numel()} (the scales in ws)")
+    return ws_num
+
+
+def _packed(packed, N, K):
+    import torch
+    _require(packed, torch.uint8, "packed", bl_packed_bytes(N, K))
 
 
 # ---------------------------------------------------------------------------
@@ -123,11 +153,13 @@ def bl_packed_bytes(N: int, K: int) -> int:
 def pack_ternary_weights(w, n_invalid=None):
     """Pack an int8 N x K ternary matrix (device) into the 16x256-tile layout (uint8 tensor)."""
     import torch
+    if w.dim() != 2:
+        raise ValueError("w must be an N x K matrix")
     _require(w, torch.int8, "w")
     N, K = w.shape
+    _optional(n_invalid, torch.int32, "n_invalid", 1)
+    _on_device(w=w, n_invalid=n_invalid)
     packed = torch.empty(bl_packed_bytes(N, K), dtype=torch.uint8, device=w.device)
-    if n_invalid is not None:
-        _require(n_invalid, torch.int32, "n_invalid")
     _check(lib().pack_ternary_weights(_ptr(w), _ptr(packed), N, K, _ptr(n_invalid), _stream()),
            "pack_ternary_weights")
     return packed
@@ -151,8 +183,12 @@ def ternarize_weights_absmean(w, workspace=None):
     ``workspace`` (uint8, TERNARIZE_WORKSPACE_BYTES) is allocated when not given.
     """
     import torch
+    if w.dim() != 2:
+        raise ValueError("w must be an N x K matrix")
     _require(w, torch.bfloat16, "w")
     N, K = w.shape
+    _optional(workspace, torch.uint8, "workspace", TERNARIZE_WORKSPACE_BYTES)
+    _on_device(w=w, workspace=workspace)
     packed = torch.empty(bl_packed_bytes(N, K), dtype=torch.uint8, device=w.device)
     scales = torch.empty(3, dtype=torch.bfloat16, device=w.device)
     if workspace is None:
@@ -168,6 +204,7 @@ def quantize_act_absmax_i8(x):
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("x must be float32 or bfloat16")
     _require(x, x.dtype, "x")
+    _on_device(x=x)
     x2 = x.reshape(-1, x.shape[-1])
     M, K = x2.shape
     q = torch.empty((M, K), dtype=torch.int8, device=x.device)
@@ -185,21 +222,17 @@ def bitlinear_i8xi2(xq, packed, s, ws, N, ws_num=None, y=None, acc=None):
     """
     import torch
     _require(xq, torch.int8, "xq")
-    _require(packed, torch.uint8, "packed")
-    _require(s, torch.float32, "s")
-    _require(ws, torch.bfloat16, "ws")
     xq2 = xq.reshape(-1, xq.shape[-1])
     M, K = xq2.shape
-    ws_num = ws.numel() if ws_num is None else ws_num
-    if packed.numel() != bl_packed_bytes(N, K):
-        raise ValueError("packed has the wrong size for (N, K)")
-    if s.numel() != M:
-        raise ValueError("s must have one scale per row")
+    _packed(packed, N, K)
+    _require(s, torch.float32, "s", M)
+    _require(ws, torch.bfloat16, "ws")
+    ws_num = _ws_num(ws, ws_num)
+    _optional(y, torch.bfloat16, "y", M * N)
+    _optional(acc, torch.int32, "acc", M * N)
+    _on_device(xq=xq, packed=packed, s=s, ws=ws, y=y, acc=acc)
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
-    _require(y, torch.bfloat16, "y")
-    if acc is not None:
-        _require(acc, torch.int32, "acc")
     _check(lib().bitlinear_i8xi2(_ptr(xq2), _ptr(packed), _ptr(s), _ptr(ws), ws_num, _ptr(y),
                                  _ptr(acc), M, N, K, _stream()), "bitlinear_i8xi2")
     return y
@@ -209,21 +242,19 @@ def bitlinear_lut_i8xi2(xq, packed, s, ws, N, ws_num=None, y=None, acc=None):
     """The M = 1 layer by table lookup: int8 xq (K), packed weights, fp32 s (1), bf16 ws ->
     bf16 y (N); the same bits as bitlinear_i8xi2 (a second algorithm, K <= LUT_MAX_K)."""
     import torch
-    _require(xq, torch.int8, "xq")
-    _require(packed, torch.uint8, "packed")
-    _require(s, torch.float32, "s")
-    _require(ws, torch.bfloat16, "ws")
     K = xq.shape[-1]
-    if xq.numel() != K or s.numel() != 1:
+    if xq.numel() != K:
         raise ValueError("bitlinear_lut_i8xi2 takes one activation row")
-    ws_num = ws.numel() if ws_num is None else ws_num
-    if packed.numel() != bl_packed_bytes(N, K):
-        raise ValueError("packed has the wrong size for (N, K)")
+    _require(xq, torch.int8, "xq")
+    _packed(packed, N, K)
+    _require(s, torch.float32, "s", 1)
+    _require(ws, torch.bfloat16, "ws")
+    ws_num = _ws_num(ws, ws_num)
+    _optional(y, torch.bfloat16, "y", N)
+    _optional(acc, torch.int32, "acc", N)
+    _on_device(xq=xq, packed=packed, s=s, ws=ws, y=y, acc=acc)
     if y is None:
         y = torch.empty((N,), dtype=torch.bfloat16, device=xq.device)
-    _require(y, torch.bfloat16, "y")
-    if acc is not None:
-        _require(acc, torch.int32, "acc")
     _check(lib().bitlinear_lut_i8xi2(_ptr(xq), _ptr(packed), _ptr(s), _ptr(ws), ws_num, _ptr(y),
                                      _ptr(acc), N, K, _stream()), "bitlinear_lut_i8xi2")
     return y
@@ -237,13 +268,16 @@ def bitlinear_bf16_i8xi2(x, packed, ws, N, ws_num=None, y=None, q_out=None, s_ou
     """
     import torch
     _require(x, torch.bfloat16, "x")
-    _require(packed, torch.uint8, "packed")
-    _require(ws, torch.bfloat16, "ws")
     x2 = x.reshape(-1, x.shape[-1])
     M, K = x2.shape
-    ws_num = ws.numel() if ws_num is None else ws_num
-    if packed.numel() != bl_packed_bytes(N, K):
-        raise ValueError("packed has the wrong size for (N, K)")
+    _packed(packed, N, K)
+    _require(ws, torch.bfloat16, "ws")
+    ws_num = _ws_num(ws, ws_num)
+    _optional(y, torch.bfloat16, "y", M * N)
+    _optional(q_out, torch.int8, "q_out", M * K)
+    _optional(s_out, torch.float32, "s_out", M)
+    _optional(acc, torch.int32, "acc", M * N)
+    _on_device(x=x, packed=packed, ws=ws, y=y, q_out=q_out, s_out=s_out, acc=acc)
     if (M > 1 or K > GEMV_MAX_K) and q_out is None:
         q_out = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if (M > 1 or K > GEMV_MAX_K) and s_out is None:
@@ -262,15 +296,20 @@ def bitlinear_rmsnorm_i8xi2(x, packed, gamma, ws, N, ws_num=None, x_up=None, res
     per-token int8 quantisation -> the layer -> [+ residual].  Returns y (bf16, N)."""
     import torch
     _require(x, torch.bfloat16, "x")
-    _require(gamma, torch.bfloat16, "gamma")
-    _require(packed, torch.uint8, "packed")
-    _require(ws, torch.bfloat16, "ws")
     K = x.numel()
-    ws_num = ws.numel() if ws_num is None else ws_num
-    if packed.numel() != bl_packed_bytes(N, K):
-        raise ValueError("packed has the wrong size for (N, K)")
-    if gamma.numel() != K or (x_up is not None and x_up.numel() != K):
-        raise ValueError("gamma and x_up must have K elements")
+    _optional(x_up, torch.bfloat16, "x_up", K)
+    _require(gamma, torch.bfloat16, "gamma", K)
+    _packed(packed, N, K)
+    _require(ws, torch.bfloat16, "ws")
+    ws_num = _ws_num(ws, ws_num)
+    _optional(residual, torch.bfloat16, "residual", N)
+    _optional(y, torch.bfloat16, "y", N)
+    _optional(xn_out, torch.bfloat16, "xn_out", K)
+    _optional(q_out, torch.int8, "q_out", K)
+    _optional(s_out, torch.float32, "s_out", 1)
+    _optional(acc, torch.int32, "acc", N)
+    _on_device(x=x, x_up=x_up, gamma=gamma, packed=packed, ws=ws, residual=residual, y=y,
+               xn_out=xn_out, q_out=q_out, s_out=s_out, acc=acc)
     if y is None:
         y = torch.empty((N,), dtype=torch.bfloat16, device=x.device)
     _check(lib().bitlinear_rmsnorm_i8xi2(_ptr(x), _ptr(x_up), _ptr(gamma), float(eps),
@@ -289,6 +328,17 @@ class DecodeGraph:
     """
 
     def __init__(self, calls):
+        import torch
+        for i, c in enumerate(calls):
+            N, K = c["N"], c["K"]
+            _require(c["x"], torch.bfloat16, f"calls[{i}].x", K)
+            _packed(c["packed"], N, K)
+            _require(c["ws"], torch.bfloat16, f"calls[{i}].ws")
+            _ws_num(c["ws"], c["ws_num"])
+            _require(c["y"], torch.bfloat16, f"calls[{i}].y", N)
+            _optional(c.get("acc"), torch.int32, f"calls[{i}].acc", N)
+        for i, c in enumerate(calls):
+            _on_device(**{f"calls[{i}].{k}": c.get(k) for k in ("x", "packed", "ws", "y", "acc")})
         self._keep = calls
         arr = (bl_gemv_desc * len(calls))()
         for i, c in enumerate(calls):
@@ -302,6 +352,11 @@ class DecodeGraph:
 
     def __len__(self):
         return lib().bl_graph_size(self._h)
+
+    @property
+    def kernels(self):
+        """Kernel launches per replay (independent calls share a grouped launch)."""
+        return lib().bl_graph_kernels(self._h)
 
     def launch(self):
         _check(lib().bl_graph_launch(self._h, _stream()), "bl_graph_launch")
@@ -324,6 +379,20 @@ class ChainedDecodeGraph(DecodeGraph):
     each call may read an earlier call's y.  The tensors must stay alive with the graph."""
 
     def __init__(self, calls):
+        import torch
+        for i, c in enumerate(calls):
+            N, K = c["N"], c["K"]
+            _require(c["x"], torch.bfloat16, f"calls[{i}].x", K)
+            _optional(c.get("x_up"), torch.bfloat16, f"calls[{i}].x_up", K)
+            _require(c["gamma"], torch.bfloat16, f"calls[{i}].gamma", K)
+            _packed(c["packed"], N, K)
+            _require(c["ws"], torch.bfloat16, f"calls[{i}].ws")
+            _ws_num(c["ws"], c["ws_num"])
+            _optional(c.get("residual"), torch.bfloat16, f"calls[{i}].residual", N)
+            _require(c["y"], torch.bfloat16, f"calls[{i}].y", N)
+        for i, c in enumerate(calls):
+            _on_device(**{f"calls[{i}].{k}": c.get(k)
+                          for k in ("x", "x_up", "gamma", "packed", "ws", "residual", "y")})
         self._keep = calls
         arr = (bl_norm_desc * len(calls))()
 
