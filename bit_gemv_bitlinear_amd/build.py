@@ -13,11 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitlinear.so")
-# measurement aid for bench.py (not part of the layer): its own library
-PROBE_SRC = os.path.join(HERE, "probe", "stream_floor.hip")
-PROBE_LIB = os.path.join(HERE, "libstream_floor.so")
-SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "gemv_local.hip", "gemv_norm.hip",
-           "gemv_lut.hip", "gemm_mfma.hip", "gemm_prefill.hip", "ternarize.hip"]
+SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "gemv_local.hip", "gemv_group.hip",
+           "gemv_norm.hip", "gemv_lut.hip", "gemm_mfma.hip", "gemm_prefill.hip", "ternarize.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -70,9 +67,6 @@ def build(verbose: bool = False) -> str:
         out_tmp = LIB + ".tmp"
         _run([HIPCC, *LDFLAGS, *objs, "-o", out_tmp], verbose)
         os.replace(out_tmp, LIB)
-        probe_tmp = PROBE_LIB + ".tmp"
-        _run([HIPCC, *FLAGS, *LDFLAGS, PROBE_SRC, "-o", probe_tmp], verbose)
-        os.replace(probe_tmp, PROBE_LIB)
     return LIB
 
 
