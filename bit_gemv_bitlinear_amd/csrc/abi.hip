@@ -9,7 +9,10 @@
 // matches; this one accepts any shape in range and returns a status code.
 #include <hip/hip_runtime.h>
 
+#include <iterator>
+#include <map>
 #include <new>
+#include <vector>
 
 #include "bitlinear.h"
 #include "kernels.hpp"
@@ -122,25 +125,36 @@ int run_layer_bf16(const uint16_t* x, const uint8_t* packed, const uint16_t* ws,
 
 struct bl_graph {
     hipGraphExec_t exec;
-    int n;
+    int n;                          // calls the graph holds
+    int kernels;                    // kernel launches per replay
+    std::vector<void*> tables;      // device work tables of its grouped launches
 };
 
 namespace {
 
-// Capture n calls (enqueue(i, stream) -> status) on an internal stream and
-// instantiate them into a bl_graph.
+void free_tables(std::vector<void*>& tables) {
+    for (void* p : tables) (void)hipFree(p);
+    tables.clear();
+}
+
+// Capture n_launch enqueue(i, stream) calls on an internal stream and
+// instantiate them into a bl_graph that also owns `tables`.
 template <class Enqueue>
-int capture_graph(int n, bl_graph** out, Enqueue enqueue) {
+int capture_graph(int n_calls, int n_launch, std::vector<void*>& tables, bl_graph** out,
+                  Enqueue enqueue) {
     (void)hipGetLastError();
     hipStream_t cs = nullptr;
-    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return BL_ERR_HIP;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) {
+        free_tables(tables);
+        return BL_ERR_HIP;
+    }
     int rc = BL_OK;
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
         rc = BL_ERR_HIP;
     } else {
-        for (int i = 0; i < n && rc == BL_OK; ++i) rc = enqueue(i, cs);
+        for (int i = 0; i < n_launch && rc == BL_OK; ++i) rc = enqueue(i, cs);
         const hipError_t e = hipStreamEndCapture(cs, &graph);
         if (rc == BL_OK && e != hipSuccess) rc = BL_ERR_HIP;
     }
@@ -150,16 +164,84 @@ int capture_graph(int n, bl_graph** out, Enqueue enqueue) {
     (void)hipStreamDestroy(cs);
     if (rc != BL_OK) {
         if (exec) (void)hipGraphExecDestroy(exec);
+        free_tables(tables);
         return rc;
     }
-    bl_graph* g = new (std::nothrow) bl_graph{exec, n};
+    bl_graph* g = new (std::nothrow) bl_graph{exec, n_calls, n_launch, {}};
     if (!g) {
         (void)hipGraphExecDestroy(exec);
+        free_tables(tables);
         return BL_ERR_ARG;
     }
+    g->tables.swap(tables);
     *out = g;
     return BL_OK;
 }
+
+// Byte ranges [lo, hi) of device memory, merged as they are added: the union
+// of what a run of calls reads, or of what it writes.
+class RangeUnion {
+  public:
+    bool overlaps(uintptr_t lo, uintptr_t hi) const {
+        if (lo >= hi) return false;
+        auto it = r_.upper_bound(lo);            // first range starting above lo
+        if (it != r_.begin() && std::prev(it)->second > lo) return true;
+        return it != r_.end() && it->first < hi;
+    }
+    void add(uintptr_t lo, uintptr_t hi) {
+        if (lo >= hi) return;
+        auto it = r_.upper_bound(lo);
+        if (it != r_.begin() && std::prev(it)->second >= lo) --it;
+        while (it != r_.end() && it->first <= hi) {
+            lo = std::min(lo, it->first);
+            hi = std::max(hi, it->second);
+            it = r_.erase(it);
+        }
+        r_.emplace(lo, hi);
+    }
+    void clear() { r_.clear(); }
+
+  private:
+    std::map<uintptr_t, uintptr_t> r_;
+};
+
+uintptr_t addr(const void* p) { return reinterpret_cast<uintptr_t>(p); }
+
+// The memory one call of the decode step reads and writes.
+struct CallRanges {
+    uintptr_t in[3][2];
+    uintptr_t out[2][2];
+};
+
+CallRanges ranges_of(const bl_gemv_desc& d) {
+    CallRanges r{};
+    r.in[0][0] = addr(d.x);
+    r.in[0][1] = addr(d.x) + 2u * static_cast<uintptr_t>(d.K);
+    r.in[1][0] = addr(d.packed);
+    r.in[1][1] = addr(d.packed) + bl::packed_bytes(d.N, d.K);
+    r.in[2][0] = addr(d.ws);
+    r.in[2][1] = addr(d.ws) + 2u * static_cast<uintptr_t>(d.ws_num);
+    r.out[0][0] = addr(d.y);
+    r.out[0][1] = addr(d.y) + 2u * static_cast<uintptr_t>(d.N);
+    r.out[1][0] = d.acc ? addr(d.acc) : 0;
+    r.out[1][1] = d.acc ? addr(d.acc) + 4u * static_cast<uintptr_t>(d.N) : 0;
+    return r;
+}
+
+bool any_overlap(const RangeUnion& u, const uintptr_t (*r)[2], int n) {
+    for (int i = 0; i < n; ++i)
+        if (u.overlaps(r[i][0], r[i][1])) return true;
+    return false;
+}
+
+// One launch of the decode-step graph: either one call on its own (the
+// single GEMV kernel) or a run of independent calls as one grouped launch.
+struct Launch {
+    int first, count;               // calls [first, first + count)
+    const bl::GroupWork* table;     // device work table of a grouped launch
+    int n_work;
+    size_t lds;
+};
 
 }  // namespace
 
@@ -264,14 +346,77 @@ int bl_graph_create(const bl_gemv_desc* descs, int n, bl_graph** out) {
     *out = nullptr;
     if (!descs) return BL_ERR_NULL;
     if (n < 1 || n > 65536) return BL_ERR_ARG;
+    std::vector<CallRanges> rng(n);
     for (int i = 0; i < n; ++i) {
         const bl_gemv_desc& d = descs[i];
         const int rc = check_layer_bf16(d.x, d.packed, d.ws, d.ws_num, d.y, nullptr, nullptr,
                                         d.acc, 1, d.N, d.K);
         if (rc) return rc;
+        rng[i] = ranges_of(d);
+        // a call's outputs may not overlap its own inputs or each other:
+        // other workgroups of the same call still read them
+        RangeUnion own;
+        for (auto& r : rng[i].in) own.add(r[0], r[1]);
+        if (any_overlap(own, rng[i].out, 2)) return BL_ERR_ARG;
+        RangeUnion y;
+        y.add(rng[i].out[0][0], rng[i].out[0][1]);
+        if (any_overlap(y, rng[i].out + 1, 1)) return BL_ERR_ARG;
     }
-    return capture_graph(n, out, [&](int i, hipStream_t cs) {
-        const bl_gemv_desc& d = descs[i];
+    // Runs of consecutive calls that neither read nor write what another call
+    // of the run writes run as one grouped launch, in any order; a call that
+    // conflicts with its run starts the next run, so the stream order keeps
+    // every dependence.
+    std::vector<Launch> launches;
+    {
+        RangeUnion reads, writes;
+        int first = 0;
+        for (int i = 0; i <= n; ++i) {
+            const bool end = (i == n) || !bl::group_supported(descs[i].K) ||
+                             (i > first && !bl::group_supported(descs[first].K)) ||
+                             any_overlap(writes, rng[i].in, 3) ||
+                             any_overlap(writes, rng[i].out, 2) ||
+                             any_overlap(reads, rng[i].out, 2);
+            if (end && i > first) {
+                launches.push_back(Launch{first, i - first, nullptr, 0, 0});
+                reads.clear();
+                writes.clear();
+                first = i;
+            }
+            if (i == n) break;
+            for (auto& r : rng[i].in) reads.add(r[0], r[1]);
+            for (auto& r : rng[i].out) writes.add(r[0], r[1]);
+        }
+    }
+    // Work tables of the grouped launches, written once here.
+    std::vector<void*> tables;
+    for (Launch& L : launches) {
+        if (L.count < 2) continue;
+        std::vector<bl::GroupWork> work;
+        for (int i = L.first; i < L.first + L.count; ++i) {
+            const bl_gemv_desc& d = descs[i];
+            bl::group_work_records(bl::GroupNode{d.x, d.packed, d.ws, d.ws_num, d.y, d.acc, d.N, d.K},
+                                   work);
+            L.lds = std::max(L.lds, bl::group_lds_bytes(d.K));
+        }
+        void* p = nullptr;
+        const size_t bytes = work.size() * sizeof(bl::GroupWork);
+        if (hipMalloc(&p, bytes) != hipSuccess) {
+            free_tables(tables);
+            return BL_ERR_HIP;
+        }
+        tables.push_back(p);
+        if (hipMemcpy(p, work.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+            free_tables(tables);
+            return BL_ERR_HIP;
+        }
+        L.table = static_cast<const bl::GroupWork*>(p);
+        L.n_work = static_cast<int>(work.size());
+    }
+    return capture_graph(n, static_cast<int>(launches.size()), tables, out,
+                         [&](int li, hipStream_t cs) {
+        const Launch& L = launches[li];
+        if (L.table) return status_of(bl::launch_gemv_group(L.table, L.n_work, L.lds, cs));
+        const bl_gemv_desc& d = descs[L.first];
         return run_layer_bf16(d.x, d.packed, d.ws, d.ws_num, d.y, nullptr, nullptr, d.acc, 1, d.N,
                               d.K, cs);
     });
@@ -288,7 +433,8 @@ int bl_graph_create_norm(const bl_norm_desc* descs, int n, bl_graph** out) {
                                   d.residual, d.y, nullptr, nullptr, nullptr, nullptr, d.N, d.K);
         if (rc) return rc;
     }
-    return capture_graph(n, out, [&](int i, hipStream_t cs) {
+    std::vector<void*> none;
+    return capture_graph(n, n, none, out, [&](int i, hipStream_t cs) {
         const bl_norm_desc& d = descs[i];
         return status_of(bl::launch_gemv_norm(d.x, d.x_up, d.gamma, d.eps, d.packed, d.ws,
                                               d.ws_num, d.residual, d.y, nullptr, nullptr,
@@ -303,9 +449,12 @@ int bl_graph_launch(bl_graph* graph, hipStream_t stream) {
 
 int bl_graph_size(const bl_graph* graph) { return graph ? graph->n : BL_ERR_NULL; }
 
+int bl_graph_kernels(const bl_graph* graph) { return graph ? graph->kernels : BL_ERR_NULL; }
+
 int bl_graph_destroy(bl_graph* graph) {
     if (!graph) return BL_OK;
     const hipError_t e = hipGraphExecDestroy(graph->exec);
+    free_tables(graph->tables);
     delete graph;
     return status_of(e);
 }

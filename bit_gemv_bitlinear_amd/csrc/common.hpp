@@ -22,6 +22,16 @@ constexpr uint32_t kCodeToInt8 = 0x0100FF00u;
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
+// A pointer into the global address space.  Kernels that read their pointers
+// from a record in memory (not from kernel arguments) cast them with global()
+// so that the compiler emits global rather than flat loads and stores.
+template <class T>
+using global_ptr = __attribute__((address_space(1))) T*;
+template <class T>
+__device__ __forceinline__ global_ptr<T> global(T* p) {
+    return (global_ptr<T>)(p);
+}
+
 __device__ __forceinline__ float bf16_to_float(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

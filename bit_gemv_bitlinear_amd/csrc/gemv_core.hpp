@@ -34,8 +34,11 @@ __device__ __forceinline__ void dot_slot(const v4u& wv, const int4& x, RowAcc& r
     dot_word(wv.w, x, r.a1[3], r.a4[3], r.a16[3]);
 }
 
-template <int P>
-__device__ __forceinline__ void load_steps(const v4u* __restrict__ tiles, int s0, int s_last,
+// Ptr: const v4u*, or a pointer into the global address space (kernels that
+// read their pointers from memory rather than kernel arguments cast them, so
+// that the loads are global rather than flat loads).
+template <int P, class Ptr>
+__device__ __forceinline__ void load_steps(Ptr __restrict__ tiles, int s0, int s_last,
                                            v4u (&w)[P]) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {

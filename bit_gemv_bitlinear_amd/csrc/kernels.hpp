@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace bl {
 
 size_t packed_bytes(int N, int K);
@@ -54,6 +56,39 @@ hipError_t launch_gemv_local(const uint16_t* x, const uint8_t* packed, const uin
                              uint32_t seg_mul, int seg_shift, uint16_t* y, int32_t* acc,
                              int8_t* q_out, float* s_out, int N, int K, unsigned groups,
                              int waves, int steps, int lw, hipStream_t stream);
+
+// Grouped GEMV: many independent M == 1 bf16 calls in one launch, one
+// 64-byte work record per workgroup (4 bands of one node).  K <= kGroupMaxK.
+struct GroupNode {
+    const uint16_t* x;
+    const uint8_t* packed;
+    const uint16_t* ws;
+    int ws_num;
+    uint16_t* y;
+    int32_t* acc;
+    int N;
+    int K;
+};
+struct alignas(64) GroupWork {
+    const void* packed;        // the node's packed weights
+    const uint16_t* x;         // its bf16 activation row
+    const uint16_t* ws;        // its weight scales
+    uint16_t* y;               // its output row
+    int32_t* acc;              // or null
+    int N;
+    int K;
+    uint32_t seg_mul;          // weight-scale segment of row n: (n * seg_mul) >> seg_shift
+    int seg_shift;
+    int group;                 // the workgroup's index within its node
+    int pad;
+};
+static_assert(sizeof(GroupWork) == 64, "one 64-byte record per workgroup");
+constexpr int kGroupMaxK = 10240;  // four chunks of ten 256-K tiles
+bool group_supported(int K);
+int group_workgroups(int N);
+size_t group_lds_bytes(int K);
+void group_work_records(const GroupNode& node, std::vector<GroupWork>& out);
+hipError_t launch_gemv_group(const GroupWork* work, int n_work, size_t lds, hipStream_t stream);
 
 // M == 1, int8 activations, by table lookup (a cross-check of the dot-product
 // GEMV); K <= kLutMaxK.

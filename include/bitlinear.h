@@ -28,9 +28,10 @@
  *   - The caller owns every buffer and keeps it alive until the work on
  *     `stream` (or the graph that captured it) has completed.
  *   - No call allocates or frees device memory except bl_graph_create /
- *     bl_graph_destroy (graph objects) and the library holds no global
- *     state, so calls on different streams may run concurrently when their
- *     outputs do not overlap.
+ *     bl_graph_destroy (graph objects and their work tables), so calls on
+ *     different streams may run concurrently when their outputs do not
+ *     overlap.  The only state the library keeps is the table-lookup GEMV's
+ *     once-per-device raise of its kernels' LDS limit.
  *   - Alignment: xq, x, packed and q_out 16 bytes; s, s_out, acc 4 bytes;
  *     ws, y 2 bytes.  Otherwise BL_ERR_ALIGN.
  *   - Shapes: 1 <= M <= 1048576, N >= 1, K >= 16 with K % 16 == 0,
@@ -264,8 +265,14 @@ int bitlinear_rmsnorm_i8xi2(const uint16_t* x, const uint16_t* x_up, const uint1
 /*
  * Decode-step graph ([W2A8] §六 item 1: each decode step is a graph
  * replay).  A bl_gemv_desc is one M = 1 call of bitlinear_bf16_i8xi2; the
- * graph chains n of them in array order (each depends on the previous one)
- * and is replayed with one launch.
+ * graph runs n of them with the results of running them in array order, and
+ * is replayed with one launch.  Consecutive calls that do not touch what
+ * another of them writes (no call reads or writes another's y or acc) form
+ * a run, and a run of two or more calls with K <= 10240 is one grouped
+ * kernel launch: each of its workgroups takes four 16-row bands of one call.
+ * A call that reads or overwrites an earlier call's output starts a new
+ * run, so it sees that output.  The results are bit-identical to the calls
+ * one by one.
  */
 typedef struct bl_gemv_desc {
     const uint16_t* x;       /* device, bf16, K */
@@ -282,11 +289,15 @@ typedef struct bl_graph bl_graph;
 
 /*
  * Capture the n calls (1 <= n <= 65536; every descriptor K <= 61440) on an
- * internal stream and instantiate them.  The descriptors are validated first; the pointers they
- * hold are baked into the graph and must stay valid while it exists.
- * *out receives the graph (NULL on error).
- * Errors: BL_ERR_NULL, BL_ERR_ARG (n), any error of bitlinear_bf16_i8xi2
- * for an invalid descriptor, BL_ERR_HIP.
+ * internal stream of its own (this call takes no stream) and instantiate
+ * them.  The descriptors are validated first; the pointers they hold are
+ * baked into the graph and must stay valid while it exists.  The work
+ * tables of the grouped launches (64 bytes per workgroup) are allocated in
+ * device memory here, filled by a synchronous copy, and freed by
+ * bl_graph_destroy.  *out receives the graph (NULL on error).
+ * Errors: BL_ERR_NULL, BL_ERR_ARG (n; a call whose y or acc overlaps its own
+ * x, packed or ws, or whose y and acc overlap), any error of
+ * bitlinear_bf16_i8xi2 for an invalid descriptor, BL_ERR_HIP.
  */
 int bl_graph_create(const bl_gemv_desc* descs, int n, bl_graph** out);
 
@@ -318,6 +329,9 @@ int bl_graph_launch(bl_graph* graph, hipStream_t stream);
 
 /* Number of calls the graph holds, or BL_ERR_NULL. */
 int bl_graph_size(const bl_graph* graph);
+
+/* Number of kernel launches one replay of the graph makes, or BL_ERR_NULL. */
+int bl_graph_kernels(const bl_graph* graph);
 
 /* Destroy the graph (NULL is allowed).  The caller ensures no replay is in flight. */
 int bl_graph_destroy(bl_graph* graph);
