@@ -7,17 +7,22 @@ in the W2A8 page, "BitNet GPU æŽ¨ç†æ¡†æž¶ï¼šä»Žé›¶æž„å»º W2A8 çš„ 2-bit å¤§æ¨¡å
 å†…æ ¸", Â§ä¸€ and Â§7.1), reported as microseconds per GEMV and achieved HBM
 GB/s against MI355X's 8 TB/s.
 
-Method:
+Method (the same for every launch-per-step workload):
   * inputs are seeded synthetic data of the page's shapes (module ``synth``),
     resident in HBM before timing starts;
-  * the packed weights are replicated into enough copies (>= 512 MiB in
-    total) that consecutive GEMVs never find their weights in the 256 MiB
-    Infinity Cache or the 4 MiB L2s; launch i reads copy i % copies;
-  * the K timed launches are captured in one HIP graph, bracketed by HIP
-    events recorded on the stream the graph runs on, after W untimed
-    warm-up launches and one untimed replay of the same graph (a graph's
-    first replay runs every launch slower; a decode loop replays its graph
-    once per token);
+  * the packed weights are replicated into n >= 2 copies of >= 512 MiB in
+    total, and every launch -- warm-up, untimed and timed alike -- reads the
+    next copy of one continuing rotation: a timed launch's weights were last
+    read n launches (>= 512 MiB of other weights) earlier, so neither the
+    256 MiB Infinity Cache nor the 4 MiB L2s hold them;
+  * K = --steps launches are captured in one HIP graph and 2K in another;
+    each timed replay is preceded by an untimed prefix graph of 2n launches
+    (the GPU is busy with it while the host submits the timed graph, so
+    submission falls outside the timed region) and bracketed by HIP events
+    recorded on the stream the graphs run on;
+  * per launch = median over repetitions of (t(2K) - t(K)) / K: whatever a
+    replay costs once (the events, the graph's first packet) cancels; the
+    direct t(K) / K is reported beside it;
   * bytes per GEMV = N*K/4 (packed weights) + M*K (int8 x) + 2*M*N (bf16 y)
     + 4*M (s) + 2*ws_num (ws) -- the algorithmic bytes, each read once.
 
@@ -27,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -47,7 +53,6 @@ PROFILE_PMC = os.path.join(ROOT, "profiles", "gemv_i8_13824x2560_pmc.txt")
 GEMV_SOURCES = [os.path.join(ROOT, "bit_gemv_bitlinear_amd", "csrc", f)
                 for f in ("gemv.hip", "gemv_core.hpp", "common.hpp")] + \
                [os.path.join(ROOT, "bit_gemv_bitlinear_amd", "build.py")]
-PROBE_LIB = os.path.join(ROOT, "bit_gemv_bitlinear_amd", "libstream_floor.so")
 
 
 def gemv_bytes(M, N, K, ws_num, x_bytes=1):
@@ -76,42 +81,132 @@ def replicate(packed, n):
     return [out[i] for i in range(n)]
 
 
-def time_graph(launch, steps, warmup):
-    """Average ms per launch of `steps` launches captured in one graph (after `warmup` launches).
+def reps_for(steps):
+    """Timed repetitions: enough that a short --steps still gives a steady median."""
+    return max(5, min(41, -(-20000 // max(steps, 1))))
 
-    The timed graph is replayed once, untimed, before the timed replay: on this runtime a
-    graph's first replay runs every launch slower than later replays (measured same box:
-    13824 x 2560 int8 3.43 against 3.32 us, bf16 input 4.14 against 3.63 us), and a decode
-    loop replays its graph once per token.  Uploading the graph beforehand (hipGraphUpload)
-    does not remove that cost."""
+
+def _capture(launch, first, count):
+    torch = _torch()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(first, first + count):
+            launch(i)
+    return g
+
+
+def time_launches(launch, n_copies, steps, warmup):
+    """Per-launch time in ms of launch(i) (launch i reads weight copy i % n_copies).
+
+    Graphs of `steps` and 2 * `steps` launches, each replay after an untimed prefix graph of
+    2 * n_copies launches; both start at copy 0, which the prefix last read n_copies launches
+    before its end, so the rotation never breaks.  Returns (slope, direct, detail)."""
     torch = _torch()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for i in range(min(warmup, 8)):
+        for i in range(max(warmup, 1)):
             launch(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    if warmup > 8:
-        gw = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gw):
-            for i in range(warmup - 8):
-                launch(i)
-        gw.replay()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(steps):
-            launch(i)
-    g.replay()
+    L = steps
+    pre = _capture(launch, 0, 2 * n_copies)
+    g1 = _capture(launch, 0, L)
+    g2 = _capture(launch, 0, 2 * L)
+    for g in (pre, g1, pre, g2, pre):       # a graph's first replay runs slower
+        g.replay()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    slopes, direct, pre_ms, host_ms = [], [], [], []
+    for _ in range(reps_for(L)):
+        torch.cuda.synchronize()
+        ev[0].record()
+        pre.replay()
+        ev[1].record()
+        h0 = time.perf_counter()
+        g1.replay()
+        h1 = time.perf_counter()
+        ev[2].record()
+        pre.replay()
+        ev[3].record()
+        g2.replay()
+        ev[4].record()
+        torch.cuda.synchronize()
+        t1 = ev[1].elapsed_time(ev[2])
+        t2 = ev[3].elapsed_time(ev[4])
+        slopes.append((t2 - t1) / L)
+        direct.append(t1 / L)
+        pre_ms.append(ev[0].elapsed_time(ev[1]))
+        host_ms.append((h1 - h0) * 1e3)
+    slope = statistics.median(slopes)
+    d = statistics.median(direct)
+    detail = {"reps": len(slopes), "direct_us": round(d * 1e3, 3),
+              "prefix_gpu_ms": round(statistics.median(pre_ms), 3),
+              "host_submit_ms": round(statistics.median(host_ms), 3)}
+    return slope, d, detail
+
+
+def time_replays(replay, reps):
+    """Per-replay ms of a whole-step graph: (t(2R) - t(R)) / R, each after untimed replays."""
+    torch = _torch()
+    for _ in range(3):
+        replay()
     torch.cuda.synchronize()
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    out = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        replay()                            # untimed: busy while the timed replays are submitted
+        ev[0].record()
+        for _ in range(reps):
+            replay()
+        ev[1].record()
+        replay()
+        ev[2].record()
+        for _ in range(2 * reps):
+            replay()
+        ev[3].record()
+        torch.cuda.synchronize()
+        out.append((ev[2].elapsed_time(ev[3]) - ev[0].elapsed_time(ev[1])) / reps)
+    return statistics.median(out)
+
+
+def rotating_layer(bl, c, steps, warmup, lut=False):
+    """Time bitlinear_i8xi2 (or the table-lookup GEMV) on int8 instance c with rotating weights."""
+    torch = _torch()
+    packed = bl.pack_ternary_weights(torch.from_numpy(c.w).cuda())
+    n_copies = copies_for(packed.numel())
+    copies = replicate(packed, n_copies)
+    ptrs = [p.data_ptr() for p in copies]
+    xq = torch.from_numpy(np.ascontiguousarray(c.xq)).cuda()
+    s = torch.from_numpy(c.s).cuda()
+    ws = bf16_dev(c.ws)
+    y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+    lib = bl.lib()
+
+    def launch(i):
+        st = torch.cuda.current_stream().cuda_stream
+        if lut:
+            rc = lib.bitlinear_lut_i8xi2(xq.data_ptr(), ptrs[i % n_copies], s.data_ptr(),
+                                         ws.data_ptr(), c.ws_num, y.data_ptr(), None, c.N, c.K, st)
+        else:
+            rc = lib.bitlinear_i8xi2(xq.data_ptr(), ptrs[i % n_copies], s.data_ptr(), ws.data_ptr(),
+                                     c.ws_num, y.data_ptr(), None, c.M, c.N, c.K, st)
+        if rc != 0:
+            raise RuntimeError(f"layer launch failed: {rc}")
+
+    slope, direct, detail = time_launches(launch, n_copies, steps, warmup)
+    detail["weight_copies"] = n_copies
+    del copies
+    return slope, direct, detail
+
+
+def gemv_entry(ms, nbytes, extra=None):
+    e = {"us": round(ms * 1e3, 3), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+         "pct_of_peak_hbm": round(100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)}
+    if extra:
+        e.update(extra)
+    return e
 
 
 # ---------------------------------------------------------------------------
@@ -120,28 +215,9 @@ def time_graph(launch, steps, warmup):
 
 def headline(bl, steps, warmup):
     """M=1 GEMV, N=13824, K=2560, ws_num=2, int8 uniform activations."""
-    torch = _torch()
     c = synth.layer("gate_up")
-    packed = bl.pack_ternary_weights(torch.from_numpy(c.w).cuda())
-    n_copies = copies_for(packed.numel())
-    copies = replicate(packed, n_copies)
-    xq = torch.from_numpy(c.xq).cuda()
-    s = torch.from_numpy(c.s).cuda()
-    ws = bf16_dev(c.ws)
-    y = torch.empty((1, c.N), dtype=torch.bfloat16, device="cuda")
-    lib = bl.lib()
-    args = [xq.data_ptr(), None, s.data_ptr(), ws.data_ptr(), c.ws_num, y.data_ptr(), None, 1,
-            c.N, c.K]
-    ptrs = [p.data_ptr() for p in copies]
-
-    def launch(i):
-        args[1] = ptrs[i % n_copies]
-        rc = lib.bitlinear_i8xi2(*args, torch.cuda.current_stream().cuda_stream)
-        if rc != 0:
-            raise RuntimeError(f"bitlinear_i8xi2 failed: {rc}")
-
-    ms = time_graph(launch, steps, warmup)
-    return c, ms, n_copies, copies
+    slope, direct, detail = rotating_layer(bl, c, steps, warmup)
+    return c, slope, detail
 
 
 def fused(bl, steps, warmup):
@@ -164,103 +240,80 @@ def fused(bl, steps, warmup):
         if rc != 0:
             raise RuntimeError(f"bitlinear_bf16_i8xi2 failed: {rc}")
 
-    ms = time_graph(launch, steps, warmup)
-    return ms
+    slope, _, _ = time_launches(launch, n_copies, steps, warmup)
+    return gemv_entry(slope, gemv_bytes(1, 13824, 2560, 2, x_bytes=2))
 
 
 def layer_shapes(bl, steps, warmup, lut=False):
     """The int8 layer set through bitlinear_i8xi2, or through the table-lookup GEMV
     (bitlinear_lut_i8xi2, the cross-check algorithm) when lut is set."""
+    out = {}
+    for c in synth.layer_set():
+        slope, _, _ = rotating_layer(bl, c, steps, warmup, lut=lut)
+        out[f"{c.name}_{c.N}x{c.K}"] = gemv_entry(slope, gemv_bytes(1, c.N, c.K, c.ws_num))
+    return out
+
+
+def large_shapes(bl, steps, warmup):
+    """The large M=1 shapes (55296x5120, 13824x5120, 5120x13824): sparse ternary weights
+    (P(0) = 1/2), activations quantised from x ~ N(0, 1) by the device quantiser."""
     torch = _torch()
     out = {}
-    lib = bl.lib()
-    for c in synth.layer_set():
-        packed = bl.pack_ternary_weights(torch.from_numpy(c.w).cuda())
-        n_copies = copies_for(packed.numel())
-        copies = replicate(packed, n_copies)
-        ptrs = [p.data_ptr() for p in copies]
-        xq = torch.from_numpy(c.xq).cuda()
-        s = torch.from_numpy(c.s).cuda()
-        ws = bf16_dev(c.ws)
-        y = torch.empty((1, c.N), dtype=torch.bfloat16, device="cuda")
-
-        def launch(i, c=c, xq=xq, s=s, ws=ws, y=y, ptrs=ptrs, n_copies=n_copies):
-            st = torch.cuda.current_stream().cuda_stream
-            if lut:
-                rc = lib.bitlinear_lut_i8xi2(xq.data_ptr(), ptrs[i % n_copies], s.data_ptr(),
-                                             ws.data_ptr(), c.ws_num, y.data_ptr(), None, c.N,
-                                             c.K, st)
-            else:
-                rc = lib.bitlinear_i8xi2(xq.data_ptr(), ptrs[i % n_copies], s.data_ptr(),
-                                         ws.data_ptr(), c.ws_num, y.data_ptr(), None, 1, c.N, c.K,
-                                         st)
-            if rc != 0:
-                raise RuntimeError(f"layer launch failed: {rc}")
-
-        ms = time_graph(launch, steps, warmup)
-        b = gemv_bytes(1, c.N, c.K, c.ws_num)
-        out[f"{c.name}_{c.N}x{c.K}"] = {"us": round(ms * 1e3, 3),
-                                        "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
-        del copies
+    for cf in synth.large_set():
+        q, s = bl.quantize_act_absmax_i8(torch.from_numpy(cf.x).cuda())
+        torch.cuda.synchronize()
+        c = synth.Gemv(cf.name, 1, cf.N, cf.K, cf.ws_num, cf.w, q.cpu().numpy(), s.cpu().numpy(),
+                       cf.ws)
+        slope, _, detail = rotating_layer(bl, c, steps, warmup)
+        out[f"{cf.N}x{cf.K}"] = gemv_entry(slope, gemv_bytes(1, cf.N, cf.K, cf.ws_num),
+                                           {"weight_copies": detail["weight_copies"]})
     return out
 
 
 def batched(bl, steps, warmup, ms=synth.BATCHED_M):
     torch = _torch()
     out = {}
-    lib = bl.lib()
     for M in ms:
-        c = synth.batched(M)
-        packed = bl.pack_ternary_weights(torch.from_numpy(c.w).cuda())
-        n_copies = copies_for(packed.numel())
-        copies = replicate(packed, n_copies)
-        ptrs = [p.data_ptr() for p in copies]
-        q, s = bl.quantize_act_absmax_i8(torch.from_numpy(c.x).cuda())
-        ws = bf16_dev(c.ws)
-        y = torch.empty((M, c.N), dtype=torch.bfloat16, device="cuda")
-
-        def launch(i, c=c, q=q, s=s, ws=ws, y=y, ptrs=ptrs, n_copies=n_copies, M=M):
-            rc = lib.bitlinear_i8xi2(q.data_ptr(), ptrs[i % n_copies], s.data_ptr(), ws.data_ptr(),
-                                     c.ws_num, y.data_ptr(), None, M, c.N, c.K,
-                                     torch.cuda.current_stream().cuda_stream)
-            if rc != 0:
-                raise RuntimeError(f"bitlinear_i8xi2 failed: {rc}")
-
-        ms = time_graph(launch, steps, warmup)
-        b = gemv_bytes(M, c.N, c.K, c.ws_num)
+        cf = synth.batched(M)
+        q, s = bl.quantize_act_absmax_i8(torch.from_numpy(cf.x).cuda())
+        torch.cuda.synchronize()
+        c = synth.Gemv(cf.name, M, cf.N, cf.K, cf.ws_num, cf.w, q.cpu().numpy(), s.cpu().numpy(),
+                       cf.ws)
+        slope, _, _ = rotating_layer(bl, c, steps, warmup)
         ops = 2.0 * M * c.N * c.K
-        out[f"M{M}"] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
-                        "mfma_util": round(ops / (ms * 1e-3) / (PEAK_INT8_TOPS * 1e12), 4)}
-        del copies
+        out[f"M{M}"] = gemv_entry(slope, gemv_bytes(M, c.N, c.K, c.ws_num),
+                                  {"mfma_util": round(ops / (slope * 1e-3) / (PEAK_INT8_TOPS * 1e12), 4)})
     return out
 
 
 def ternarize(bl, steps, warmup):
     """Weight ternarisation + packing of a bf16 13824 x 2560 matrix ([W2A8] Â§4.2): one call
-    = exponent histogram, finalise, ternarise-and-pack.  Four rotating weight copies (283 MB)."""
+    = exponent histogram, finalise, ternarise-and-pack.  Rotating bf16 weight copies."""
     torch = _torch()
     N, K = 13824, 2560
     g = synth.rng(synth.seed_for(9, 1, 0))
     w = bf16_dev(synth.weights_bf16(g, N, K))
-    copies = [w] + [w.clone() for _ in range(3)]
+    n_copies = copies_for(2 * N * K)
+    copies = [w] + [w.clone() for _ in range(n_copies - 1)]
     packed = torch.empty(bl.bl_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
     scales = torch.empty(3, dtype=torch.bfloat16, device="cuda")
     work = torch.empty(bl.TERNARIZE_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
     lib = bl.lib()
 
     def launch(i):
-        rc = lib.ternarize_weights_absmean(copies[i % 4].data_ptr(), packed.data_ptr(),
+        rc = lib.ternarize_weights_absmean(copies[i % n_copies].data_ptr(), packed.data_ptr(),
                                            scales.data_ptr(), work.data_ptr(), N, K,
                                            torch.cuda.current_stream().cuda_stream)
         if rc != 0:
             raise RuntimeError(f"ternarize_weights_absmean failed: {rc}")
 
-    ms = time_graph(launch, steps, warmup)
+    slope, _, _ = time_launches(launch, n_copies, steps, warmup)
     b = 2 * (2 * N * K) + N * K // 4 + 2048 + 6   # bf16 read twice, packed written
-    return {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": b}
+    del copies
+    return {"us": round(slope * 1e3, 3), "GBps": round(b / (slope * 1e-3) / 1e9, 1), "bytes": b}
 
 
-def decode_step(bl, reps):
+def decode_step(bl):
     """30 layers x {qkv, o, gate+up, down}, fused quantisation, one bl_graph per step."""
     torch = _torch()
     calls = []
@@ -271,23 +324,15 @@ def decode_step(bl, reps):
                           N=c.N, K=c.K))
     nbytes = sum(gemv_bytes(1, c["N"], c["K"], c["ws_num"], x_bytes=2) for c in calls)
     g = bl.DecodeGraph(calls)
-    for _ in range(3):
-        g.launch()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(reps):
-        g.launch()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / reps
+    ms = time_replays(g.launch, 10)
+    kernels = g.kernels
     g.close()
     return {"us_per_step": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "bytes_per_step": nbytes, "gemvs_per_step": len(calls)}
+            "pct_of_peak_hbm": round(100.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 1),
+            "bytes_per_step": nbytes, "gemvs_per_step": len(calls), "kernels_per_step": kernels}
 
 
-def chained_step(bl, reps):
+def chained_step(bl):
     """The decode step chained through its glue (readings of the norms and MLP activation the
     pages name): 30 layers x {qkv after attention_norm, o after attn_sub_norm + residual,
     gate+up after ffn_norm, down after relu(gate)^2 * up and ffn_sub_norm + residual}; one
@@ -322,20 +367,12 @@ def chained_step(bl, reps):
         nbytes += 2 * c["K"] * (2 if c.get("x_up") is not None else 1) - 2 * c["K"]
         nbytes += 2 * c["K"] + (2 * c["N"] if c.get("residual") is not None else 0)
     g = bl.ChainedDecodeGraph(calls)
-    for _ in range(3):
-        g.launch()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(reps):
-        g.launch()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / reps
+    ms = time_replays(g.launch, 10)
+    kernels = g.kernels
     g.close()
     return {"us_per_step": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "bytes_per_step": nbytes, "projections_per_step": len(calls)}
+            "bytes_per_step": nbytes, "projections_per_step": len(calls),
+            "kernels_per_step": kernels}
 
 
 def torch_bf16_context(steps):
@@ -351,32 +388,92 @@ def torch_bf16_context(steps):
     def launch(i):
         torch.matmul(x, ws[i % n_copies].t(), out=outs)
 
-    ms = time_graph(launch, steps, 16)
-    return {"us": round(ms * 1e3, 3)}
+    slope, _, _ = time_launches(launch, n_copies, steps, 16)
+    return {"us": round(slope * 1e3, 3)}
 
 
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle, as it stands
 # ---------------------------------------------------------------------------
 
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    """Threads for the all-cores leg: the cores this process may run on, within the
+    OMP_NUM_THREADS share when one is set."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(n, 1)
+
+
+def _oracle_gemv_threads(c, threads):
+    """One full GEMV as `threads` slices of rows, each an unchanged oracle call (the oracle's C
+    runs without the interpreter lock, so the slices run in parallel).  Slices stay inside
+    one weight-scale segment."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    seg = c.N // c.ws_num
+    per_seg = max(1, threads // c.ws_num)
+    parts = []
+    for sgi in range(c.ws_num):
+        bounds = np.linspace(sgi * seg, (sgi + 1) * seg, per_seg + 1).astype(int)
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            parts.append((a, b, c.ws[sgi:sgi + 1]))
+    ex = ThreadPoolExecutor(max_workers=threads)
+
+    def one(p):
+        a, b, ws = p
+        return oracle.bitlinear_i8(c.xq, c.w[a:b], c.s, ws, 1)
+
+    def run():
+        return list(ex.map(one, parts))
+    return run, ex, parts
+
+
 def cpu_baseline(seconds):
     import oracle
     c = synth.layer("gate_up")
-    oracle.bitlinear_i8(c.xq, c.w, c.s, c.ws, c.ws_num)     # load + warm
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.bitlinear_i8(c.xq, c.w, c.s, c.ws, c.ws_num)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per = el / n
     b = gemv_bytes(1, c.N, c.K, c.ws_num)
-    return {"value": round(b / per / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "us_per_gemv": round(per * 1e6, 1),
-            "sample": f"{n} full M=1 GEMVs at N=13824 K=2560 (int8 x, unpacked ternary w, int64 "
-                      f"sums, fp64 epilogue), single-threaded C, {el:.1f} s"}
+    oracle.bitlinear_i8(c.xq, c.w, c.s, c.ws, c.ws_num)     # load + warm
+
+    def timed(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return el / n, n, el
+
+    per1, n1, el1 = timed(lambda: oracle.bitlinear_i8(c.xq, c.w, c.s, c.ws, c.ws_num))
+    threads = host_threads()
+    run, ex, parts = _oracle_gemv_threads(c, threads)
+    # the slices together are the whole GEMV: same int32 sums and bf16 outputs
+    whole = oracle.bitlinear_i8(c.xq, c.w, c.s, c.ws, c.ws_num)[1].reshape(-1)
+    got = np.concatenate([r[1].reshape(-1) for r in run()])
+    if not np.array_equal(got, whole):
+        raise RuntimeError("threaded oracle slices disagree with the whole oracle GEMV")
+    perT, nT, elT = timed(run)
+    ex.shutdown()
+    return {"value": round(b / perT / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "us_per_gemv": round(perT * 1e6, 1),
+            "host_cpu": host_cpu_model(), "host_cpus_available": os.cpu_count(),
+            "sample": f"{nT} full M=1 GEMVs at N=13824 K=2560 in {elT:.1f} s, each as {len(parts)} "
+                      f"row slices on {threads} threads (the unchanged single-threaded C oracle per "
+                      f"slice: int8 x, unpacked ternary w, int64 sums, fp64 epilogue)",
+            "single_core": {"value": round(b / per1 / 1e9, 3), "unit": "GB/s",
+                            "us_per_gemv": round(per1 * 1e6, 1),
+                            "sample": f"{n1} full GEMVs, one thread, {el1:.1f} s"}}
 
 
 def gemv_source_sha256():
@@ -418,36 +515,7 @@ def gemv_geometry(N, K):
     return B, B * Wb, P
 
 
-def stream_floor(copies, N, K, steps, warmup):
-    """Same launch shape and bytes as the GEMV: an empty launch and a pure streaming read."""
-    import ctypes
-    torch = _torch()
-    lib = ctypes.CDLL(PROBE_LIB)
-    P_ = ctypes.c_void_p
-    I_ = ctypes.c_int
-    lib.stream_floor_empty.argtypes = [I_, I_, P_, P_]
-    lib.stream_floor_read.argtypes = [P_, I_, I_, I_, I_, I_, P_, P_]
-    nbands, S = -(-N // 16), -(-K // 256)
-    B, W, P = gemv_geometry(N, K)
-    groups = -(-nbands // B)
-    out = torch.zeros(groups, dtype=torch.int32, device="cuda")
-    ptrs = [c.data_ptr() for c in copies]
-
-    def empty(i):
-        if lib.stream_floor_empty(groups, W, out.data_ptr(), torch.cuda.current_stream().cuda_stream):
-            raise RuntimeError("stream_floor_empty failed")
-
-    def read(i):
-        if lib.stream_floor_read(ptrs[i % len(ptrs)], nbands, S, B, W, P, out.data_ptr(),
-                                 torch.cuda.current_stream().cuda_stream):
-            raise RuntimeError("stream_floor_read failed")
-
-    e_ms = time_graph(empty, steps, warmup)
-    r_ms = time_graph(read, steps, warmup)
-    nbytes = nbands * S * 1024
-    return {"launch_shape": f"{groups} workgroups x {W} wavefronts ({B} bands), {P} 16-byte loads per lane",
-            "empty_launch_us": round(e_ms * 1e3, 3), "stream_read_us": round(r_ms * 1e3, 3),
-            "stream_read_GBps": round(nbytes / (r_ms * 1e-3) / 1e9, 1)}
+ALL_SECTIONS = "fused,layer_set,large,lut,batched,prefill,decode_step,chained_step,ternarize,torch"
 
 
 def main():
@@ -456,17 +524,19 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only")
-    ap.add_argument("--sections",
-                    default="fused,layer_set,lut,batched,prefill,decode_step,chained_step,ternarize,torch",
+    ap.add_argument("--sections", default=ALL_SECTIONS,
                     help="detail sections to run after the headline (comma list; for profiling one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain copy of 256 MiB (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the layer is not sharded across GPUs in this build)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        print("--steps must be at least 1", file=sys.stderr)
         sys.exit(2)
 
     torch = _torch()
@@ -475,15 +545,10 @@ def main():
         sys.exit(2)
     import bit_gemv_bitlinear_amd as bl
 
-    c, ms, n_copies, copies = headline(bl, args.steps, args.warmup)
+    c, ms, hdetail = headline(bl, args.steps, args.warmup)
     nbytes = gemv_bytes(1, c.N, c.K, c.ws_num)
     gbs = nbytes / (ms * 1e-3) / 1e9
     detail = {}
-    if os.path.exists(PROBE_LIB) and not args.pmc_calibrate:
-        fl = stream_floor(copies, c.N, c.K, args.steps, args.warmup)
-        fl["gemv_us_over_stream_read_us"] = round(ms * 1e3 / fl["stream_read_us"], 3)
-        detail["single_launch_floor_13824x2560"] = fl
-    del copies
     if args.pmc_calibrate:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -492,29 +557,31 @@ def main():
         torch.cuda.synchronize()
         detail["calibration_copy_bytes"] = 256 << 20
     sections = set() if args.quick else set(args.sections.split(","))
+    short = min(args.steps, 400)
     if "fused" in sections:
-        fms = fused(bl, max(args.steps // 2, 100), min(args.warmup, 100))
-        fb = gemv_bytes(1, 13824, 2560, 2, x_bytes=2)
-        detail["fused_bf16_13824x2560"] = {"us": round(fms * 1e3, 3),
-                                           "GBps": round(fb / (fms * 1e-3) / 1e9, 1)}
+        detail["fused_bf16_13824x2560"] = fused(bl, short, 20)
     if "layer_set" in sections:
-        detail["layer_set_int8"] = layer_shapes(bl, max(args.steps // 4, 100), 50)
+        detail["layer_set_int8"] = layer_shapes(bl, short, 20)
+    if "large" in sections:
+        detail["large_int8"] = large_shapes(bl, min(args.steps, 100), 10)
     if "lut" in sections:
-        detail["layer_set_int8_lut"] = layer_shapes(bl, max(args.steps // 4, 100), 50, lut=True)
+        detail["layer_set_int8_lut"] = layer_shapes(bl, short, 20, lut=True)
     if "batched" in sections:
-        detail["batched_mfma"] = batched(bl, max(args.steps // 8, 50), 20)
+        detail["batched_mfma"] = batched(bl, short, 20)
     if "prefill" in sections:
-        detail["prefill_13824x2560"] = batched(bl, 50, 10, synth.PREFILL_M)
+        detail["prefill_13824x2560"] = batched(bl, min(args.steps, 100), 10, synth.PREFILL_M)
     if "decode_step" in sections:
-        detail["decode_step_graph"] = decode_step(bl, 20)
+        detail["decode_step_graph"] = decode_step(bl)
     if "chained_step" in sections:
-        detail["chained_decode_step_graph"] = chained_step(bl, 20)
+        detail["chained_decode_step_graph"] = chained_step(bl)
     if "ternarize" in sections:
-        detail["ternarize_pack_bf16_13824x2560"] = ternarize(bl, 50, 10)
+        detail["ternarize_pack_bf16_13824x2560"] = ternarize(bl, min(args.steps, 50), 5)
     if "torch" in sections:
-        detail["torch_bf16_matmul_13824x2560"] = torch_bf16_context(200)
+        detail["torch_bf16_matmul_13824x2560"] = torch_bf16_context(min(args.steps, 200))
 
     traffic = pmc_traffic()
+    B, W, P = gemv_geometry(c.N, c.K)
+    groups = -(-(-(-c.N // 16)) // B)        # ceil(ceil(N / 16) / B)
     line = {
         "metric": "M=1 W2A8 GEMV Âµs + achieved HBM GB/s (% of peak) at N=13824,K=2560",
         "value": round(gbs, 1),
@@ -534,8 +601,14 @@ def main():
         "config": {"workload": "M=1 W2A8 GEMV N=13824 K=2560 (gate+up of a 2B-style layer), "
                                "uniform ternary weights, uniform int8 activations, ws_num=2",
                    "M": 1, "N": c.N, "K": c.K, "ws_num": c.ws_num,
-                   "bytes_per_gemv": nbytes, "weight_copies": n_copies,
-                   "timing": "one HIP graph of `steps` launches after one untimed replay of it, HIP events on its stream"},
+                   "bytes_per_gemv": nbytes, "weight_copies": hdetail["weight_copies"],
+                   "launch": f"{groups} workgroups x {W} wavefronts, "
+                             f"{P} K-steps per wavefront",
+                   "timing": "per launch = median over reps of (t(2*steps) - t(steps)) / steps, "
+                             "graphs of steps and 2*steps launches each after an untimed prefix of "
+                             "2*copies launches, HIP events on the graphs' stream; every launch "
+                             "reads the next weight copy of one rotation",
+                   "timing_detail": hdetail},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
