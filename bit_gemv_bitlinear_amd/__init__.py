@@ -36,6 +36,7 @@ SIGNATURES = {
     "pack_ternary_weights": (_I, [_P, _P, _I, _I, _P, _P]),
     "bl_pack_ternary_host": (ctypes.c_int64, [_P, _P, _I, _I]),
     "ternarize_weights_absmean": (_I, [_P, _P, _P, _P, _I, _I, _P]),
+    "ternarize_weights_absmean_noalloc": (_I, [_P, _P, _P, _I, _I, _P]),
     "quantize_act_absmax_i8": (_I, [_P, _I, _P, _P, _I, _I, _P]),
     "bitlinear_i8xi2": (_I, [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _P]),
     "bitlinear_bf16_i8xi2": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _P]),

@@ -290,6 +290,20 @@ int ternarize_weights_absmean(const uint16_t* w, uint8_t* packed, uint16_t* scal
     return status_of(bl::launch_ternarize(w, packed, scales, workspace, N, K, stream));
 }
 
+int ternarize_weights_absmean_noalloc(const uint16_t* w, uint8_t* packed, uint16_t* scales,
+                                      int N, int K, hipStream_t stream) {
+    if (!w || !packed || !scales) return BL_ERR_NULL;
+    const int rc = check_mnk(1, N, K);
+    if (rc) return rc;
+    if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(scales, 2)) return BL_ERR_ALIGN;
+    static_assert(BL_TERNARIZE_WORKSPACE_BYTES <= bl::kTernarizeScratchBytes,
+                  "the library-held histogram holds the workspace of any matrix");
+    (void)hipGetLastError();
+    void* hist = nullptr;
+    if (bl::ternarize_scratch(&hist) != hipSuccess) return BL_ERR_HIP;
+    return status_of(bl::launch_ternarize(w, packed, scales, hist, N, K, stream));
+}
+
 int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int M, int K,
                            hipStream_t stream) {
     if (!x || !q || !s) return BL_ERR_NULL;

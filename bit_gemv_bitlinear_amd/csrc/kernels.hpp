@@ -109,6 +109,10 @@ hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* x_up, const uint1
 // ws, s, mean (bf16); workspace: 256 uint64 (the exponent histogram).
 hipError_t launch_ternarize(const uint16_t* w, uint8_t* packed, uint16_t* scales,
                             void* workspace, int N, int K, hipStream_t stream);
+// Device address, on the current device, of the ternariser's library-held
+// histogram (kTernarizeScratchBytes), for the allocation-free entry point.
+constexpr size_t kTernarizeScratchBytes = 2048;
+hipError_t ternarize_scratch(void** out);
 
 // Many activation rows (prompt processing), int8 activations, int8 MFMA
 // with LDS-tiled reuse of both operands.

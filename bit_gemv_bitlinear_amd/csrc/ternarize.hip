@@ -25,6 +25,8 @@
 //     and ws;
 //   * ternarize_pack_kernel: one thread per packed 32-bit word reads its 16
 //     bf16 weights and writes the word, like the int8 packer.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -302,6 +304,41 @@ hipError_t launch_ternarize(const uint16_t* w, uint8_t* packed, uint16_t* scales
     ternarize_pack_kernel<<<static_cast<unsigned>((n_words + 255) / 256), 256, 0, stream>>>(
         w, reinterpret_cast<uint32_t*>(packed), scales, N, K, S, n_words);
     return hipGetLastError();
+}
+
+// The histogram of the allocation-free entry point, for callers that cannot
+// allocate: one 2 KiB array per GPU, held by the library until the process
+// ends.  Its 256 bins serve a matrix of any size.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): the address comes from hipGetSymbolAddress, once per device.
+// Every call on a GPU shares that GPU's array; the first kernel of a call
+// clears it, and calls that overlap on one GPU race.
+static __device__ __align__(256) unsigned long long scratch[kBins];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void* scratch_addr[kMaxDevices];
+hipError_t scratch_status[kMaxDevices];
+
+}  // namespace
+
+hipError_t ternarize_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    // with device `dev` current: each GPU holds its own copy of the array
+    std::call_once(scratch_once[dev], [dev] {
+        void* p = nullptr;
+        scratch_status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        scratch_addr[dev] = p;
+    });
+    if (scratch_status[dev] != hipSuccess) return scratch_status[dev];
+    if (scratch_addr[dev] == nullptr) return hipErrorInvalidSymbol;
+    *out = scratch_addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace bl

@@ -146,6 +146,24 @@ int ternarize_weights_absmean(const uint16_t* w, uint8_t* packed, uint16_t* scal
                               void* workspace, int N, int K, hipStream_t stream);
 
 /*
+ * ternarize_weights_absmean_noalloc -- ternarize_weights_absmean without the
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under graph capture, serving loops that forbid allocation).  The same
+ * kernels and bits; the histogram lives in a 2 KiB array the library holds
+ * on each GPU it runs on until the process ends (its address is looked up
+ * once per device, on the first call with that device current).  The array
+ * serves a matrix of any size the layer accepts, so no shape exceeds it;
+ * shapes outside the layer's limits return BL_ERR_SHAPE.  The call itself
+ * allocates nothing.  Every call on a GPU shares that GPU's array: the call
+ * clears it first, and calls that overlap on one GPU (several streams, or
+ * replays in flight together) race and give undefined results.
+ *   w, packed, scales, N, K as ternarize_weights_absmean.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP.
+ */
+int ternarize_weights_absmean_noalloc(const uint16_t* w, uint8_t* packed, uint16_t* scales,
+                                      int N, int K, hipStream_t stream);
+
+/*
  * quantize_act_absmax_i8 -- per-token (per-row) absmax int8 quantisation
  * ([W2A8] §六 item 3):
  *   s[m]    = 127 / max(max_k |x[m][k]|, 1e-5)          fp32, IEEE division
