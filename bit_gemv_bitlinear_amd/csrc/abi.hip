@@ -9,6 +9,7 @@
 // matches; this one accepts any shape in range and returns a status code.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <iterator>
 #include <map>
 #include <new>
@@ -441,15 +442,116 @@ int bl_graph_create_norm(const bl_norm_desc* descs, int n, bl_graph** out) {
     *out = nullptr;
     if (!descs) return BL_ERR_NULL;
     if (n < 1 || n > 65536) return BL_ERR_ARG;
+    // What each call reads (x, x_up, gamma, packed, ws, residual) and writes (y).
+    struct NormRanges {
+        uintptr_t in[6][2];
+        uintptr_t out[1][2];
+    };
+    std::vector<NormRanges> rng(n);
     for (int i = 0; i < n; ++i) {
         const bl_norm_desc& d = descs[i];
         const int rc = check_norm(d.x, d.x_up, d.gamma, d.eps, d.packed, d.ws, d.ws_num,
                                   d.residual, d.y, nullptr, nullptr, nullptr, nullptr, d.N, d.K);
         if (rc) return rc;
+        const uintptr_t K2 = 2u * static_cast<uintptr_t>(d.K), N2 = 2u * static_cast<uintptr_t>(d.N);
+        NormRanges& r = rng[i];
+        r.in[0][0] = addr(d.x), r.in[0][1] = addr(d.x) + K2;
+        r.in[1][0] = d.x_up ? addr(d.x_up) : 0, r.in[1][1] = d.x_up ? addr(d.x_up) + K2 : 0;
+        r.in[2][0] = addr(d.gamma), r.in[2][1] = addr(d.gamma) + K2;
+        r.in[3][0] = addr(d.packed), r.in[3][1] = addr(d.packed) + bl::packed_bytes(d.N, d.K);
+        r.in[4][0] = addr(d.ws), r.in[4][1] = addr(d.ws) + 2u * static_cast<uintptr_t>(d.ws_num);
+        r.in[5][0] = d.residual ? addr(d.residual) : 0;
+        r.in[5][1] = d.residual ? addr(d.residual) + N2 : 0;
+        r.out[0][0] = addr(d.y), r.out[0][1] = addr(d.y) + N2;
+        // y may be the residual itself (each output reads only its own
+        // residual) but may overlap no other input of its call
+        RangeUnion own;
+        for (int k = 0; k < 5; ++k) own.add(r.in[k][0], r.in[k][1]);
+        if (any_overlap(own, r.out, 1)) return BL_ERR_ARG;
+        if (d.residual && d.residual != d.y) {
+            RangeUnion res;
+            res.add(r.in[5][0], r.in[5][1]);
+            if (any_overlap(res, r.out, 1)) return BL_ERR_ARG;
+        }
     }
-    std::vector<void*> none;
-    return capture_graph(n, n, none, out, [&](int i, hipStream_t cs) {
+    // Runs of independent calls (as in bl_graph_create); inside a run, the
+    // calls of one kernel instance share a grouped launch.
+    struct NormLaunch {
+        std::vector<int> calls;
+        bl::NormPlan key;
+        const bl::NormWork* table;
+        int n_work;
+        size_t lds;
+    };
+    std::vector<NormLaunch> launches;
+    auto same_instance = [](const bl::NormPlan& a, const bl::NormPlan& b) {
+        return a.glu == b.glu && a.cached == b.cached && a.steps == b.steps && a.threads == b.threads;
+    };
+    std::vector<bl::NormPlan> plans(n);
+    for (int i = 0; i < n; ++i) {
         const bl_norm_desc& d = descs[i];
+        plans[i] = bl::norm_plan(d.x, d.x_up, d.gamma, d.eps, d.packed, d.ws, d.ws_num, d.residual,
+                                 d.y, nullptr, nullptr, nullptr, nullptr, d.N, d.K);
+        if (plans[i].groups == 0) return BL_ERR_SHAPE;
+    }
+    {
+        RangeUnion reads, writes;
+        int first = 0;
+        for (int i = 0; i <= n; ++i) {
+            const bool end = (i == n) || any_overlap(writes, rng[i].in, 6) ||
+                             any_overlap(writes, rng[i].out, 1) || any_overlap(reads, rng[i].out, 1);
+            if (end && i > first) {
+                std::vector<NormLaunch> run;
+                for (int j = first; j < i; ++j) {
+                    auto it = std::find_if(run.begin(), run.end(), [&](const NormLaunch& L) {
+                        return same_instance(L.key, plans[j]);
+                    });
+                    if (it == run.end()) run.push_back(NormLaunch{{j}, plans[j], nullptr, 0, 0});
+                    else it->calls.push_back(j);
+                }
+                for (auto& L : run) launches.push_back(std::move(L));
+                reads.clear();
+                writes.clear();
+                first = i;
+            }
+            if (i == n) break;
+            for (auto& r : rng[i].in) reads.add(r[0], r[1]);
+            writes.add(rng[i].out[0][0], rng[i].out[0][1]);
+        }
+    }
+    std::vector<void*> tables;
+    for (NormLaunch& L : launches) {
+        if (L.calls.size() < 2) continue;
+        std::vector<bl::NormWork> work;
+        for (int j : L.calls) {
+            for (int g = 0; g < plans[j].groups; ++g) {
+                bl::NormWork w{};
+                w.a = plans[j].args;
+                w.group = g;
+                work.push_back(w);
+            }
+            L.lds = std::max(L.lds, plans[j].lds);
+        }
+        void* p = nullptr;
+        const size_t bytes = work.size() * sizeof(bl::NormWork);
+        if (hipMalloc(&p, bytes) != hipSuccess) {
+            free_tables(tables);
+            return BL_ERR_HIP;
+        }
+        tables.push_back(p);
+        if (hipMemcpy(p, work.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+            free_tables(tables);
+            return BL_ERR_HIP;
+        }
+        L.table = static_cast<const bl::NormWork*>(p);
+        L.n_work = static_cast<int>(work.size());
+    }
+    return capture_graph(n, static_cast<int>(launches.size()), tables, out,
+                         [&](int li, hipStream_t cs) {
+        const NormLaunch& L = launches[li];
+        if (L.table)
+            return status_of(bl::launch_gemv_norm_group(L.key, L.table, L.n_work, L.lds, cs));
+        const bl_norm_desc& d = descs[L.calls[0]];
         return status_of(bl::launch_gemv_norm(d.x, d.x_up, d.gamma, d.eps, d.packed, d.ws,
                                               d.ws_num, d.residual, d.y, nullptr, nullptr,
                                               nullptr, nullptr, d.N, d.K, cs));

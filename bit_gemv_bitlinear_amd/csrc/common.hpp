@@ -21,6 +21,7 @@ constexpr uint32_t kCodeToInt8 = 0x0100FF00u;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 // A pointer into the global address space.  Kernels that read their pointers
 // from a record in memory (not from kernel arguments) cast them with global()

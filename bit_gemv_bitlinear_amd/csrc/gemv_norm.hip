@@ -167,6 +167,8 @@ __device__ __forceinline__ uint4 norm8(const double (&p)[8], double inv) {
     return bf16x8_from_f64(v);
 }
 
+__device__ __forceinline__ uint4 to_uint4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
 // A row of K bf16 values as a raw buffer (16-byte loads by chunk index).
 using RowBuf = __amdgpu_buffer_rsrc_t;
 constexpr int kRawBufferFlags = 0x00020000;   // word 3 of the descriptor: 32-bit data format
@@ -183,19 +185,21 @@ __device__ __forceinline__ uint4 row_load(RowBuf r, int chunk) {
 // budget.
 constexpr int kNormMaxWaves = 8;
 
+// One workgroup's bands of one projection: the body of the single-call kernel
+// (group = its block index) and of the grouped kernel (group = the index in
+// its work record).  The pointers are cast to the global address space: the
+// grouped kernel reads them from memory, not from its kernel arguments.
 template <int P, int C, bool GLU>
-__global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ x_up,
-    const uint16_t* __restrict__ gamma, double eps, const v4u* __restrict__ packed,
-    const uint16_t* __restrict__ ws, uint32_t seg_mul, int seg_shift,
-    const uint16_t* __restrict__ residual, uint16_t* __restrict__ y, int32_t* __restrict__ acc,
-    int8_t* __restrict__ q_out, float* __restrict__ s_out, uint16_t* __restrict__ xn_out, int N,
-    int K, int B, int lw) {
+__device__ __forceinline__ void norm_body(const NormArgs& a, int group) {
     extern __shared__ int4 act[];   // Wb*P*16 16-byte chunks: the int8 row, zero-padded
     __shared__ int part_sh[kNormMaxWaves][64];
     __shared__ int xsum_sh[kNormMaxWaves];
     __shared__ double ssq_sh[kNormMaxWaves];
     __shared__ uint32_t pm_sh[kNormMaxWaves];
+    const int N = a.N;
+    const int K = a.K;
+    const int B = a.B;
+    const int lw = a.lw;
     const int Wb = 1 << lw;
     const int W = B << lw;
     const int nthreads = W * 64;
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nbands = (N + kTileRows - 1) / kTileRows;
-    const int band = min(static_cast<int>(blockIdx.x) * B + (wave >> lw), nbands - 1);
+    const int band = min(group * B + (wave >> lw), nbands - 1);
     const int S = (K + kTileK - 1) / kTileK;
     const int s0 = (wave & (Wb - 1)) * P;
     const int n16 = K >> 4;
@@ -212,19 +216,19 @@ __global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(
 
     // 1. The inputs of this thread's output row (weight scale, residual),
     //    the cached chunks of the row (x, x_up, gamma), then every weight load.
-    const int n_out = static_cast<int>(blockIdx.x) * B * kTileRows + tid;   // tid < 16*B writes
+    const int n_out = group * B * kTileRows + tid;   // tid < 16*B writes
     const uint32_t n_c = static_cast<uint32_t>(min(n_out, N - 1));
-    const uint16_t wsb = ws[(static_cast<uint64_t>(n_c) * seg_mul) >> seg_shift];
+    const uint16_t wsb = global(a.ws)[(static_cast<uint64_t>(n_c) * a.seg_mul) >> a.seg_shift];
     // unconditional (a branch would end in a wait for this load); the weight
     // scales stand in as a source when there is no residual
-    const uint16_t resb = (residual ? residual : ws)[residual ? n_c : 0u];
-    const uint4* x16 = reinterpret_cast<const uint4*>(x);
-    const uint4* u16 = reinterpret_cast<const uint4*>(x_up);
-    const uint4* g16 = reinterpret_cast<const uint4*>(gamma);
+    const uint16_t resb = global(a.residual ? a.residual : a.ws)[a.residual ? n_c : 0u];
+    const global_ptr<const v4u> x16 = global(reinterpret_cast<const v4u*>(a.x));
+    const global_ptr<const v4u> u16 = global(reinterpret_cast<const v4u*>(a.x_up));
+    const global_ptr<const v4u> g16 = global(reinterpret_cast<const v4u*>(a.gamma));
     // The cached chunks come through buffer loads: the compiler treats plain
     // loads of these read-only rows as free to sink to their first use,
     // past the weight loads, and a wait there would wait for every one.
-    const RowBuf rx = row_buffer(x, K), ru = row_buffer(x_up, K), rg = row_buffer(gamma, K);
+    const RowBuf rx = row_buffer(a.x, K), ru = row_buffer(a.x_up, K), rg = row_buffer(a.gamma, K);
     // A chunk past the row's end reads as zeros (the buffer's range check),
     // which add nothing to the sum of squares or the maximum.
     uint4 xv[C], uv[GLU ? C : 1], gv[C];
@@ -235,7 +239,8 @@ __global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(
         if constexpr (GLU) uv[c] = row_load(ru, idx);
         gv[c] = row_load(rg, idx);
     }
-    const v4u* tiles = packed + static_cast<size_t>(band) * S * 64 + lane;
+    const global_ptr<const v4u> tiles =
+        global(reinterpret_cast<const v4u*>(a.packed)) + static_cast<size_t>(band) * S * 64 + lane;
     v4u w[P];
     load_steps<P>(tiles, s0, S - 1, w);
     // No load may move below this point (a row load sunk past the weight
@@ -252,8 +257,8 @@ __global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(
             if constexpr (GLU) return glu8(xv[c], uv[c]);
             return xv[c];
         }
-        if constexpr (GLU) return glu8(x16[idx], u16[idx]);
-        return x16[idx];
+        if constexpr (GLU) return glu8(to_uint4(x16[idx]), to_uint4(u16[idx]));
+        return to_uint4(x16[idx]);
     };
     double ssq = 0.0;
     uint32_t pm = 0;   // high word of the largest |p|
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(
     for (int c = 0; c < C; ++c) products8(m_chunk(c, tid + c * nthreads), gv[c], pv[c], ssq, pm);
     for (int idx = tid + C * nthreads; idx < n_in; idx += nthreads) {
         double pt[8];
-        products8(m_chunk(C, idx), g16[idx], pt, ssq, pm);
+        products8(m_chunk(C, idx), to_uint4(g16[idx]), pt, ssq, pm);
     }
     ssq = wave_sum_f64(ssq);
     pm = wave_max_u32(pm);
@@ -285,21 +290,21 @@ __global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(
         total_sq += i < W ? v : 0.0;
         pm = max(pm, i < W ? u : 0u);
     }
-    const double inv = 1.0 / sqrt(total_sq / static_cast<double>(K) + eps);
+    const double inv = 1.0 / sqrt(total_sq / static_cast<double>(K) + a.eps);
     const double pmax = __hiloint2double(static_cast<int>(pm), 0);
     const float amax = __uint_as_float(bf16_rne_f64(pmax * inv) << 16);
     const float sm = 127.0f / fmaxf(amax, 1e-5f);
 
     // 4. Quantise xn into LDS (workgroup 0 also writes xn, q and s when asked).
     uint2* act8 = reinterpret_cast<uint2*>(act);
-    const bool first = blockIdx.x == 0;
+    const bool first = group == 0;
     int xs = 0;
     auto put = [&](int idx, const uint4& v) {
         const uint2 o = quant8_bf16(v, sm);
         act8[idx] = o;
         xs = sum_i8x4(o.x, sum_i8x4(o.y, xs));
-        if (first && q_out) reinterpret_cast<uint2*>(q_out)[idx] = o;
-        if (first && xn_out) reinterpret_cast<uint4*>(xn_out)[idx] = v;
+        if (first && a.q_out) global(reinterpret_cast<v2u*>(a.q_out))[idx] = v2u{o.x, o.y};
+        if (first && a.xn_out) global(reinterpret_cast<v4u*>(a.xn_out))[idx] = v4u{v.x, v.y, v.z, v.w};
     };
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -308,10 +313,10 @@ __global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(
     }
     for (int idx = tid + C * nthreads; idx < n_in; idx += nthreads) {
         double pt[8];
-        products8(m_chunk(C, idx), g16[idx], pt, ssq, pm);
+        products8(m_chunk(C, idx), to_uint4(g16[idx]), pt, ssq, pm);
         put(idx, norm8(pt, inv));
     }
-    if (first && s_out != nullptr && tid == 0) s_out[0] = sm;
+    if (first && a.s_out != nullptr && tid == 0) global(a.s_out)[0] = sm;
     for (int i = n16 + tid; i < padded16; i += nthreads) act[i] = make_int4(0, 0, 0, 0);
     xs = wave_sum(xs);
     if (lane == 0) xsum_sh[wave] = xs;
@@ -345,33 +350,58 @@ __global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(
         for (int j = 0; j < Wb; ++j) total += part_sh[firstw + j][slot];
         if (bw < B && n_out < N) {
             uint16_t o = epilogue_bf16_scaled(total, cs, bf16_to_float(wsb), sm);
-            if (residual)   // the fp64 sum of two bf16 values rounds to bf16 as the exact sum does
+            if (a.residual)   // the fp64 sum of two bf16 values rounds to bf16 as the exact sum does
                 o = static_cast<uint16_t>(bf16_rne_f64(static_cast<double>(bf16_to_float(resb)) +
                                                        static_cast<double>(bf16_to_float(o))));
-            y[n_out] = o;
-            if (acc) acc[n_out] = total;
+            global(a.y)[n_out] = o;
+            if (a.acc) global(a.acc)[n_out] = total;
         }
     }
 }
 
-using GemvNormFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, double, const v4u*,
-                            const uint16_t*, uint32_t, int, const uint16_t*, uint16_t*, int32_t*,
-                            int8_t*, float*, uint16_t*, int, int, int, int);
+template <int P, int C, bool GLU>
+__global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(NormArgs a) {
+    norm_body<P, C, GLU>(a, static_cast<int>(blockIdx.x));
+}
+
+// Several projections of one kernel instance in one launch: workgroup i runs
+// the bands of work record i (its projection's arguments and its group).
+template <int P, int C, bool GLU>
+__global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_group_kernel(
+    const NormWork* __restrict__ work) {
+    const NormWork& w = work[blockIdx.x];
+    norm_body<P, C, GLU>(w.a, w.group);
+}
+
+using GemvNormFn = void (*)(NormArgs);
+using GemvNormGroupFn = void (*)(const NormWork*);
 template <int C, bool GLU, int... Ps>
 constexpr std::array<GemvNormFn, sizeof...(Ps)> norm_table(std::integer_sequence<int, Ps...>) {
     return {{&gemv_norm_kernel<Ps + 1, C, GLU>...}};
+}
+template <int C, bool GLU, int... Ps>
+constexpr std::array<GemvNormGroupFn, sizeof...(Ps)> norm_group_table(
+    std::integer_sequence<int, Ps...>) {
+    return {{&gemv_norm_group_kernel<Ps + 1, C, GLU>...}};
 }
 // P = 1 .. kNormMaxSteps (rows up to kNormMaxK over at most kNormMaxWaves
 // wavefronts per band) and C = 1 or 2 cached chunks per thread; the loop over
 // uncached chunks serves longer rows.
 constexpr int kNormMaxSteps = 16;
 using NormRow = std::array<GemvNormFn, kNormMaxSteps>;
+using NormGroupRow = std::array<GemvNormGroupFn, kNormMaxSteps>;
 // [glu][C - 1][P - 1]
 const std::array<std::array<NormRow, 2>, 2> kNormKernels = {{
     {{norm_table<1, false>(std::make_integer_sequence<int, kNormMaxSteps>{}),
       norm_table<2, false>(std::make_integer_sequence<int, kNormMaxSteps>{})}},
     {{norm_table<1, true>(std::make_integer_sequence<int, kNormMaxSteps>{}),
       norm_table<2, true>(std::make_integer_sequence<int, kNormMaxSteps>{})}},
+}};
+const std::array<std::array<NormGroupRow, 2>, 2> kNormGroupKernels = {{
+    {{norm_group_table<1, false>(std::make_integer_sequence<int, kNormMaxSteps>{}),
+      norm_group_table<2, false>(std::make_integer_sequence<int, kNormMaxSteps>{})}},
+    {{norm_group_table<1, true>(std::make_integer_sequence<int, kNormMaxSteps>{}),
+      norm_group_table<2, true>(std::make_integer_sequence<int, kNormMaxSteps>{})}},
 }};
 
 // The geometry of gemv_shape with at most kNormMaxWaves wavefronts per
@@ -391,29 +421,50 @@ GemvShape norm_shape(int N, int K) {
 
 }  // namespace
 
+NormPlan norm_plan(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma, float eps,
+                   const uint8_t* packed, const uint16_t* ws, int ws_num,
+                   const uint16_t* residual, uint16_t* y, uint16_t* xn_out, int8_t* q_out,
+                   float* s_out, int32_t* acc, int N, int K) {
+    NormPlan p{};
+    const GemvShape g = norm_shape(N, K);
+    if (g.waves == 0 || K > kNormMaxK) return p;
+    const int nbands = (N + kTileRows - 1) / kTileRows;
+    p.groups = (nbands + g.bands - 1) / g.bands;
+    const int wb = g.waves / g.bands;
+    int lw = 0;
+    while ((1 << lw) < wb) ++lw;
+    p.lds = static_cast<size_t>(wb) * g.steps * kTileK;
+    p.threads = g.waves * 64;
+    const int need = (K / 8 + p.threads - 1) / p.threads;
+    p.glu = x_up != nullptr;
+    p.cached = need <= 1 ? 1 : 2;
+    p.steps = g.steps;
+    uint32_t seg_mul;
+    int seg_shift;
+    seg_divisor(N / ws_num, seg_mul, seg_shift);
+    p.args = NormArgs{x, x_up, gamma, reinterpret_cast<const v4u*>(packed), ws, residual, y, acc,
+                      q_out, s_out, xn_out, static_cast<double>(eps), seg_mul, seg_shift, N, K,
+                      g.bands, lw};
+    return p;
+}
+
 hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma,
                             float eps, const uint8_t* packed, const uint16_t* ws, int ws_num,
                             const uint16_t* residual, uint16_t* y, uint16_t* xn_out,
                             int8_t* q_out, float* s_out, int32_t* acc, int N, int K,
                             hipStream_t stream) {
-    const GemvShape g = norm_shape(N, K);
-    if (g.waves == 0 || K > kNormMaxK) return hipErrorInvalidValue;
-    const int nbands = (N + kTileRows - 1) / kTileRows;
-    const unsigned groups = static_cast<unsigned>((nbands + g.bands - 1) / g.bands);
-    const int wb = g.waves / g.bands;
-    int lw = 0;
-    while ((1 << lw) < wb) ++lw;
-    const size_t lds = static_cast<size_t>(wb) * g.steps * kTileK;
-    const int threads = g.waves * 64;
-    const int need = (K / 8 + threads - 1) / threads;
-    const GemvNormFn fn = kNormKernels[x_up ? 1 : 0][need <= 1 ? 0 : 1][g.steps - 1];
-    uint32_t seg_mul;
-    int seg_shift;
-    seg_divisor(N / ws_num, seg_mul, seg_shift);
-    fn<<<groups, threads, lds, stream>>>(x, x_up, gamma, static_cast<double>(eps),
-                                         reinterpret_cast<const v4u*>(packed), ws, seg_mul,
-                                         seg_shift, residual, y, acc, q_out, s_out, xn_out, N, K,
-                                         g.bands, lw);
+    const NormPlan p = norm_plan(x, x_up, gamma, eps, packed, ws, ws_num, residual, y, xn_out,
+                                 q_out, s_out, acc, N, K);
+    if (p.groups == 0) return hipErrorInvalidValue;
+    const GemvNormFn fn = kNormKernels[p.glu ? 1 : 0][p.cached - 1][p.steps - 1];
+    fn<<<static_cast<unsigned>(p.groups), p.threads, p.lds, stream>>>(p.args);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_norm_group(const NormPlan& key, const NormWork* work, int n_work,
+                                  size_t lds, hipStream_t stream) {
+    const GemvNormGroupFn fn = kNormGroupKernels[key.glu ? 1 : 0][key.cached - 1][key.steps - 1];
+    fn<<<static_cast<unsigned>(n_work), key.threads, lds, stream>>>(work);
     return hipGetLastError();
 }
 

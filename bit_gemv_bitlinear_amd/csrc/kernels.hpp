@@ -105,6 +105,51 @@ hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* x_up, const uint1
                             int8_t* q_out, float* s_out, int32_t* acc, int N, int K,
                             hipStream_t stream);
 
+// The projection with its glue as a plan: its kernel instance (P = steps,
+// C = cached chunks, GLU), its launch shape and its arguments.  Projections
+// of one instance (same steps, chunks, GLU and threads) can share a grouped
+// launch: one 128-byte work record per workgroup.
+struct NormArgs {
+    const uint16_t* x;
+    const uint16_t* x_up;
+    const uint16_t* gamma;
+    const void* packed;
+    const uint16_t* ws;
+    const uint16_t* residual;
+    uint16_t* y;
+    int32_t* acc;
+    int8_t* q_out;
+    float* s_out;
+    uint16_t* xn_out;
+    double eps;
+    uint32_t seg_mul;
+    int seg_shift;
+    int N;
+    int K;
+    int B;        // bands per workgroup
+    int lw;       // log2 of the wavefronts per band
+};
+struct alignas(128) NormWork {
+    NormArgs a;
+    int group;    // the workgroup's index within its projection
+};
+static_assert(sizeof(NormWork) == 128, "one 128-byte record per workgroup");
+struct NormPlan {
+    NormArgs args;
+    int groups;   // workgroups (0: shape not supported)
+    int threads;
+    size_t lds;
+    int steps;
+    int cached;
+    bool glu;
+};
+NormPlan norm_plan(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma, float eps,
+                   const uint8_t* packed, const uint16_t* ws, int ws_num,
+                   const uint16_t* residual, uint16_t* y, uint16_t* xn_out, int8_t* q_out,
+                   float* s_out, int32_t* acc, int N, int K);
+hipError_t launch_gemv_norm_group(const NormPlan& key, const NormWork* work, int n_work,
+                                  size_t lds, hipStream_t stream);
+
 // Ternarise a bf16 N x K matrix by its mean |w| and pack it; scales[0..2] =
 // ws, s, mean (bf16); workspace: 256 uint64 (the exponent histogram).
 hipError_t launch_ternarize(const uint16_t* w, uint8_t* packed, uint16_t* scales,

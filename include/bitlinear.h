@@ -321,10 +321,16 @@ int bl_graph_create(const bl_gemv_desc* descs, int n, bl_graph** out);
 
 /*
  * A decode step chained through its glue: each bl_norm_desc is one call of
- * bitlinear_rmsnorm_i8xi2 (without the optional outputs); the graph runs
- * them in array order, so a call may read what an earlier one wrote (its
- * x, x_up or residual may be an earlier y).  Same rules and errors as
- * bl_graph_create, with bitlinear_rmsnorm_i8xi2's checks per descriptor.
+ * bitlinear_rmsnorm_i8xi2 (without the optional outputs); the graph gives
+ * the results of running them in array order, so a call may read what an
+ * earlier one wrote (its x, x_up or residual may be an earlier y).  As in
+ * bl_graph_create, consecutive calls that do not touch another's y form a
+ * run; inside a run, the calls that take the same kernel instance (the same
+ * row length class and launch shape, e.g. the qkv and o projections of a
+ * layer) share one grouped launch.  A call's y may be its own residual but
+ * may overlap none of its other inputs (BL_ERR_ARG).  Same rules and errors
+ * as bl_graph_create otherwise, with bitlinear_rmsnorm_i8xi2's checks per
+ * descriptor.
  */
 typedef struct bl_norm_desc {
     const uint16_t* x;        /* device, bf16, K */

@@ -170,6 +170,9 @@ def test_chained_two_layers_as_graph(bl):
         ]
     graph = bl.ChainedDecodeGraph(calls)
     assert len(graph) == 4 * n_layers
+    # per layer: qkv and o (independent, one kernel instance) share a launch,
+    # then gate+up, then down
+    assert graph.kernels == 3 * n_layers
     # oracle chain
     want, hb = [], h0
     for L in layers:
@@ -191,3 +194,58 @@ def test_chained_two_layers_as_graph(bl):
                 np.testing.assert_array_equal(host_bits(outs[l][k]), want[l][k],
                                               err_msg=f"replay {rep} layer {l} {k}")
     graph.close()
+
+
+def test_independent_projections_share_a_launch(bl):
+    import torch
+    # five independent calls: four of one kernel instance (rows of 2560;
+    # narrow and ragged N; one adding its residual in place) in one grouped
+    # launch, and the GLU projection of another instance on its own
+    g = synth.rng(synth.seed_for(6, 50, 0))
+    dim, ffn = synth.DIM, synth.FFN
+    specs = [("qkv", 3840, dim, 1, False, None), ("o_inplace", dim, dim, 1, False, "inplace"),
+             ("o", dim, dim, 1, False, "separate"), ("ragged", 1000, dim, 4, False, None),
+             ("down", dim, ffn, 1, True, "separate")]
+    calls, want = [], []
+    for name, N, K, wn, glu, res in specs:
+        w = synth.ternary_uniform(g, N, K)
+        ws = synth.ws_bits(g, wn)
+        x = synth.normal_bf16_bits(g, 1, K).reshape(-1)
+        up = synth.normal_bf16_bits(g, 1, K).reshape(-1) if glu else None
+        gam = oracle.bf16_rne(1.0 + 0.1 * g.normal(size=K))
+        r = synth.normal_bf16_bits(g, 1, N).reshape(-1) if res else None
+        want.append(oracle.norm_bitlinear(x, gam, w, ws, wn, up_bits=up, residual_bits=r)[4])
+        y = bf16_dev(r) if res == "inplace" else torch.full((N,), float("nan"), dtype=torch.bfloat16,
+                                                            device="cuda")
+        c = dict(x=bf16_dev(x), gamma=bf16_dev(gam), packed=bl.pack_ternary_weights(dev(w)),
+                 ws=bf16_dev(ws), ws_num=wn, y=y, N=N, K=K)
+        if glu:
+            c["x_up"] = bf16_dev(up)
+        if res == "inplace":
+            c["residual"] = y
+        elif res == "separate":
+            c["residual"] = bf16_dev(r)
+        calls.append(c)
+    print("chained graph: five independent projections", flush=True)
+    graph = bl.ChainedDecodeGraph(calls)
+    assert graph.kernels == 2
+    torch.cuda.synchronize()
+    graph.launch()
+    torch.cuda.synchronize()
+    for (name, *_), c, wv in zip(specs, calls, want):
+        np.testing.assert_array_equal(host_bits(c["y"]), wv, err_msg=name)
+    graph.close()
+
+
+def test_output_over_another_input_is_refused(bl):
+    import torch
+    g = synth.rng(synth.seed_for(6, 51, 0))
+    K = N = 256
+    w = synth.ternary_uniform(g, N, K)
+    x = bf16_dev(synth.normal_bf16_bits(g, 1, K).reshape(-1))
+    gam = bf16_dev(oracle.bf16_rne(1.0 + 0.1 * g.normal(size=K)))
+    c = dict(x=x, gamma=gam, packed=bl.pack_ternary_weights(dev(w)), ws=bf16_dev(synth.ws_bits(g, 1)),
+             ws_num=1, y=gam, N=N, K=K)
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.ChainedDecodeGraph([c])
+    assert e.value.status == bl.BL_ERR_ARG

@@ -183,11 +183,13 @@ def test_prefill_no_scratch_and_declared_lds(prefill_asm):
         assert body.count("v_mfma_i32_16x16x64_i8") == 16 * MTW, name
 
 
-def test_norm_kernels_issue_all_loads_first(norm_asm):
-    # gemv_norm_kernel<P, C, GLU>: the row's C chunks of x, gamma (and x_up),
-    # buffer loads, and all P weight tiles are issued before the first wait,
-    # without scratch
-    kernels = list(re.finditer(r"^(_ZN\S*gemv_norm_kernelILi(\d+)ELi(\d)ELb([01])E\S*):", norm_asm, re.M))
+@pytest.mark.parametrize("kind", ["gemv_norm_kernel", "gemv_norm_group_kernel"])
+def test_norm_kernels_issue_all_loads_first(norm_asm, kind):
+    # gemv_norm_kernel<P, C, GLU> (one projection) and gemv_norm_group_kernel
+    # (several, one work record per workgroup): the row's C chunks of x,
+    # gamma (and x_up), buffer loads, and all P weight tiles are issued
+    # before the first wait, without scratch
+    kernels = list(re.finditer(r"^(_ZN\S*" + kind + r"ILi(\d+)ELi(\d)ELb([01])E\S*):", norm_asm, re.M))
     assert len(kernels) == 64    # P = 1..16, C = 1, 2, with and without the GLU
     late = []
     for m in kernels:
