@@ -26,12 +26,27 @@ import numpy as np
 PATTERN = (0, 4, 8, 12, 1, 5, 9, 13, 2, 6, 10, 14, 3, 7, 11, 15)
 
 
+def _segments():
+    """The 32 row segments of a 16x32 block, in the order the page's kernel threads read
+    them (one 32-bit word, 16 consecutive K values, per thread): segment t = 16a + 8b + c
+    (a, b in {0, 1}, c in 0..7) is row 8a + c, columns 16b .. 16b + 15 -- the first 8
+    threads take rows 0-7 of the left half, the next 8 the same rows of the right half,
+    then rows 8-15 likewise.  [W2A8] §5.1 (the 16x32 permutation that lays the weights out
+    in the threads' reading order)."""
+    return [(8 * a + c, 16 * b) for a in range(2) for b in range(2) for c in range(8)]
+
+
+_SEGMENTS = _segments()
+
+
 def block_map(i: int, j: int):
-    """[W2A8] §5.1: (i, j) of a 16x32 block -> (row, col) it is read from."""
-    thread_id = i * 2 + j // 16
-    row = (thread_id // 16) * 8 + (thread_id % 8)
-    col = (j % 16) + 16 * ((thread_id % 16) // 8)
-    return row, col
+    """[W2A8] §5.1: (i, j) of a permuted 16x32 block -> (row, col) it is read from.
+
+    The permuted block holds the segments one after the other, 16 values each: its
+    position 32 i + j is value m = (32 i + j) % 16 of segment t = (32 i + j) // 16."""
+    t, m = divmod(32 * i + j, 16)
+    row, col0 = _SEGMENTS[t]
+    return row, col0 + m
 
 
 def permute(codes: np.ndarray) -> np.ndarray:

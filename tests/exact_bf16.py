@@ -85,3 +85,50 @@ def rmsnorm_exact(x_bits, g_bits, eps=EPS):
         assert best is not None
         out.append(sign | best)
     return np.array(out, dtype=np.uint16)
+
+
+def round_binary(v: Fraction, p: int, emin: int, emax: int):
+    """v rounded to the binary format with p significant bits, least normal
+    exponent emin and largest exponent emax (nearest, ties to even); None for
+    an overflow to infinity."""
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = max(e, emin) - (p - 1)
+    n = round(a / Fraction(2) ** q)          # Fraction.__round__: half to even
+    r = n * Fraction(2) ** q
+    if r >= Fraction(2) ** (emax + 1):
+        return None
+    return r if v > 0 else -r
+
+
+def r32(v):
+    return round_binary(v, 24, -126, 127)
+
+
+def r64(v):
+    return round_binary(v, 53, -1022, 1023)
+
+
+def bf16_bits(v: Fraction) -> int:
+    """bf16 encoding of v rounded to bf16 (finite results only in these cases)."""
+    r = round_binary(v, 8, -126, 127)
+    assert r is not None
+    if r == 0:
+        return 0
+    sign = 0x8000 if r < 0 else 0
+    a = abs(r)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    if e < -126:                              # subnormal: multiple of 2^-133
+        return sign | int(a / Fraction(2) ** -133)
+    mant = int(a / Fraction(2) ** (e - 7)) - 128
+    return sign | ((e + 127) << 7) | mant

@@ -2,8 +2,9 @@
 
 Checked against things other than itself: a second exact rounding routine
 (fp64-based, for values fp64 holds exactly), Fraction brute force for the
-mean, the page's own torch code on inputs where its fp32 accumulation is
-exact, closed forms, ties, the zero matrix and power-of-two scaling.
+mean, the whole definition evaluated in exact rational arithmetic with every
+rounding written out, closed forms, ties, the zero matrix and power-of-two
+scaling.
 """
 from fractions import Fraction
 
@@ -11,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+from exact_bf16 import bf16_bits, bits_to_fraction, r32
 
 
 def bits_of(values):
@@ -107,27 +109,57 @@ def test_power_of_two_scaling():
         assert f32([ws1])[0] == f32([ws0])[0] * 2.0 ** j
 
 
-def test_matches_the_pages_torch_code_where_its_sum_is_exact():
-    # The page's converter, run as written on bf16 tensors.  Inputs are
-    # multiples of 2^-8 in [-1, 1] and n = 4096, so torch's fp32 sum and its
-    # division by n are exact and its mean is the exact mean, rounded to bf16.
-    torch = pytest.importorskip("torch")
+def ternarize_by_definition(w_bits):
+    """[W2A8] §4.2 in exact arithmetic: the mean of |W| (exact, rounded once to bf16), the
+    multiplier s = 1 / max(mean, 1e-5) and the weight scale ws = 1 / s (each an fp32
+    operation rounded to bf16), Wt = clamp(round(bf16(fl32(w * s))), -1, 1) with ties to
+    even.  Every rounding is written out on Fractions (tests/exact_bf16.py)."""
+    vals = [bits_to_fraction(b) for b in np.asarray(w_bits, dtype=np.uint16).reshape(-1)]
+    mean = sum(abs(v) for v in vals) / len(vals)
+    mean_b = bf16_bits(mean)
+    m = bits_to_fraction(mean_b)
+    floor = r32(Fraction(1, 100000))                  # 1e-5 as fp32
+    if m < floor:
+        m = bits_to_fraction(bf16_bits(floor))
+    s_b = bf16_bits(r32(1 / m))
+    s = bits_to_fraction(s_b)
+    ws_b = bf16_bits(r32(1 / s))
+    q = [max(-1, min(1, round(bits_to_fraction(bf16_bits(r32(v * s)))))) for v in vals]
+    return np.array(q, dtype=np.int8).reshape(np.shape(w_bits)), mean_b, s_b, ws_b
 
-    def quant_weight_int8(weight):          # [W2A8] §4.2, as printed on the page
-        s = 1.0 / weight.abs().mean().clamp_(min=1e-5)
-        new_weight = (weight * s).round().clamp(-1, 1).to(torch.int8)
-        new_scale = (1.0 / s).to(torch.bfloat16)
-        return new_weight, new_scale.reshape(1)
 
-    g = np.random.default_rng(9)
-    for trial in range(20):
-        v = (g.integers(-256, 257, size=(64, 64)) / 256.0).astype(np.float32)
-        v *= (g.random((64, 64)) < 0.8)
+@pytest.mark.parametrize("trial", range(12))
+def test_matches_the_definition_in_exact_arithmetic(trial):
+    # random bf16 matrices over a range of magnitudes (some rows of zeros, some
+    # outliers), against the definition evaluated in exact rational arithmetic
+    g = np.random.default_rng(100 + trial)
+    N, K = 16, 48
+    scale = 2.0 ** int(g.integers(-20, 10))
+    v = (g.standard_normal((N, K)) * scale).astype(np.float32)
+    v[int(g.integers(0, N))] = 0.0
+    v[int(g.integers(0, N)), int(g.integers(0, K))] *= 50.0
+    b = (v.view(np.uint32) >> 16).astype(np.uint16)     # cut to bf16
+    want = ternarize_by_definition(b)
+    got = oracle.ternarize_absmean(b)
+    np.testing.assert_array_equal(got[0], want[0])
+    assert tuple(int(x) for x in got[1:]) == tuple(int(x) for x in want[1:])
+
+
+def test_closed_forms():
+    # all |w| equal to c: the mean is c, every w * s is about +-1 -> Wt = sign(w)
+    for c in (1.0, 0.375, 2.0 ** -9, 3.0):
+        v = np.full((16, 32), c, dtype=np.float32)
+        v[::3] *= -1.0
+        v[5] = 0.0
         b = bits_of(v)
-        wt, ws_t = quant_weight_int8(torch.from_numpy(v).to(torch.bfloat16))
         q, mean, s, ws = oracle.ternarize_absmean(b)
-        np.testing.assert_array_equal(q, wt.numpy())
-        assert ws == int(ws_t.view(torch.int16).numpy()[0]) & 0xFFFF
+        np.testing.assert_array_equal(q, np.sign(v).astype(np.int8))
+        # mean over 512 entries, a row of 32 of them zero: c * 15 / 16 (a bf16 value)
+        assert mean == int(bits_of([np.float32(c * 15 / 16)])[0])
+    # a matrix of zeros: mean 0 < 1e-5 -> s = bf16(1 / bf16(1e-5)), Wt = 0
+    q, mean, s, ws = oracle.ternarize_absmean(np.zeros((16, 32), dtype=np.uint16))
+    assert mean == 0 and not q.any()
+    assert s == bf16_bits(r32(1 / bits_to_fraction(bf16_bits(r32(Fraction(1, 100000))))))
 
 
 def test_mean_exactly_on_a_tie_and_one_subnormal_above():
