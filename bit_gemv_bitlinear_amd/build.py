@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitlinear.so")
 SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "gemv_local.hip", "gemv_group.hip",
-           "gemv_norm.hip", "gemv_lut.hip", "gemm_mfma.hip", "gemm_prefill.hip", "ternarize.hip"]
+           "gemv_norm.hip", "gemv_lut.hip", "gemm_band.hip", "gemm_mfma.hip", "gemm_prefill.hip",
+           "ternarize.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -106,6 +106,8 @@ int run_layer_i8(const int8_t* xq, const uint8_t* packed, const float* s, const 
                  int ws_num, uint16_t* y, int32_t* acc, int M, int N, int K, hipStream_t stream) {
     if (M == 1 && K <= bl::kGemvMaxK)
         return status_of(bl::launch_gemv_i8(xq, packed, s, ws, ws_num, y, acc, N, K, stream));
+    if (M >= 2 && M <= bl::kBandMaxM && K <= bl::kBandMaxK)
+        return status_of(bl::launch_gemm_band(xq, packed, s, ws, ws_num, y, acc, M, N, K, stream));
     if (M >= kPrefillMinM && N >= kPrefillMinN)
         return status_of(bl::launch_gemm_prefill(xq, packed, s, ws, ws_num, y, acc, M, N, K, stream));
     return status_of(bl::launch_gemm_mfma(xq, packed, s, ws, ws_num, y, acc, M, N, K, stream));

@@ -47,6 +47,20 @@ __device__ __forceinline__ void load_steps(Ptr __restrict__ tiles, int s0, int s
     }
 }
 
+// load_steps with the loads kept in step order (a scheduling barrier after
+// each): the waits for step u then count only the loads of steps u + 1 ..,
+// so each step can start as soon as its own tile has landed.
+template <int P, class Ptr>
+__device__ __forceinline__ void load_steps_ordered(Ptr __restrict__ tiles, int s0, int s_last,
+                                                   v4u (&w)[P]) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+        const int st = min(s0 + u, s_last);
+        w[u] = __builtin_nontemporal_load(tiles + static_cast<size_t>(st) * 64);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Each lane holds partial sums of the four rows of its 16-lane group (over
 // its own K chunk).  Afterwards lane l holds the full sum, over the 16 lanes,
 // of row l % 4 of the group: a reduce-scatter inside each quad, then a sum

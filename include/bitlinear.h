@@ -191,12 +191,15 @@ int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int 
  * The activation scale divides: s = 127/amax quantised the activations, so
  * y approximates x . w^T * ws.
  * M == 1 with K <= 61440 runs the GEMV kernel (workgroups of 1, 2 or 4
- * 16-row bands, v_dot4 on masked codes).  M >= 65 with N >= 8192 (prompt
- * processing on wide layers, the prompt lengths of [W2A8] §7.2) runs the
- * LDS-tiled int8 MFMA kernel (v_mfma_i32_16x16x64_i8; workgroup tiles of up
+ * 16-row bands, v_dot4 on masked codes).  2 <= M <= 32 with K <= 2560 (a
+ * few sequences decoded together) runs the band kernel: int8 MFMA
+ * (v_mfma_i32_16x16x64_i8), one wavefront per 16 weight rows over all of K,
+ * the activation rows staged once per workgroup in LDS.  M >= 65 with
+ * N >= 8192 (prompt processing on wide layers, the prompt lengths of
+ * [W2A8] §7.2) runs the LDS-tiled int8 MFMA kernel (workgroup tiles of up
  * to 256 weight rows x 128 activation rows reuse both operands); any other
  * M >= 2, or K > 61440, runs the int8 MFMA kernel that streams the weights
- * once per 64 rows of M.  All three give the same bits.
+ * once per 64 rows of M.  All four give the same bits.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_ARG, BL_ERR_HIP.
  */
 int bitlinear_i8xi2(const int8_t* xq, const uint8_t* packed, const float* s, const uint16_t* ws,

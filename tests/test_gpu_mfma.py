@@ -58,6 +58,17 @@ def test_shapes(bl, M, N, K):
     check(bl, c.name, c.w, c.xq, c.s, c.ws, c.ws_num)
 
 
+@pytest.mark.parametrize("M,N,K,ws_num", [(3, 16, 16, 1), (2, 1, 2560, 1), (31, 1000, 2304, 4),
+                                          (32, 13824, 2560, 2), (20, 100, 2560, 4), (9, 4096, 256, 8),
+                                          (24, 48, 1040, 3)])
+def test_band_kernel_shapes(bl, M, N, K, ws_num):
+    # 2 <= M <= 32 with K <= 2560 runs one wavefront per 16-row band: one
+    # 256-K tile or ten, a single output row, rows not filling the last
+    # workgroup, weight-scale segments that split bands, K not a multiple of 256
+    c = synth.make_int8_gemv(f"band_m{M}", M, N, K, ws_num, synth.seed_for(8, 1, M + N % 97))
+    check(bl, c.name, c.w, c.xq, c.s, c.ws, c.ws_num)
+
+
 def test_extremes_and_segments(bl):
     g = synth.rng(515)
     M, N, K = 32, 64 * 4, 2560
