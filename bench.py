@@ -375,6 +375,56 @@ def chained_step(bl):
             "kernels_per_step": kernels}
 
 
+def dispatch_probe(bl, n=400, sleep_cycles=400_000_000):
+    """The headline GEMV launched n times straight onto the stream while the GPU is held by a
+    sleep kernel (torch.cuda._sleep, a bounded spin): the launches queue up and then run back to
+    back even where submitting each one is slow (under a kernel-tracing profiler).  HIP events
+    bracket the n launches after the sleep.  Opt-in (``--sections dispatch_probe``): run under
+    ``rocprofv3 --kernel-trace``, the same process then gives both the profiler's per-dispatch
+    durations of these n back-to-back launches (the last n dispatches of the GEMV kernel) and
+    the events' per-launch time, which can be compared; without the profiler it gives the
+    per-launch time of direct (non-graph) launches."""
+    torch = _torch()
+    c = synth.layer("gate_up")
+    packed = bl.pack_ternary_weights(torch.from_numpy(c.w).cuda())
+    n_copies = copies_for(packed.numel())
+    copies = replicate(packed, n_copies)
+    ptrs = [p.data_ptr() for p in copies]
+    xq = torch.from_numpy(np.ascontiguousarray(c.xq)).cuda()
+    s = torch.from_numpy(c.s).cuda()
+    ws = bf16_dev(c.ws)
+    y = torch.empty((1, c.N), dtype=torch.bfloat16, device="cuda")
+    lib = bl.lib()
+    st = torch.cuda.current_stream()
+
+    def launch(i):
+        rc = lib.bitlinear_i8xi2(xq.data_ptr(), ptrs[i % n_copies], s.data_ptr(), ws.data_ptr(),
+                                 c.ws_num, y.data_ptr(), None, 1, c.N, c.K, st.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"layer launch failed: {rc}")
+
+    for i in range(2 * n_copies):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    torch.cuda._sleep(sleep_cycles)
+    ev[1].record()
+    h0 = time.perf_counter()
+    for i in range(n):
+        launch(i)
+    h1 = time.perf_counter()
+    ev[2].record()
+    torch.cuda.synchronize()
+    sleep_ms = ev[0].elapsed_time(ev[1])
+    run_ms = ev[1].elapsed_time(ev[2])
+    submit_ms = (h1 - h0) * 1e3
+    del copies
+    return {"launches": n, "us_per_launch": round(run_ms / n * 1e3, 3),
+            "sleep_ms": round(sleep_ms, 3), "host_submit_ms": round(submit_ms, 3),
+            "queued_before_sleep_ended": submit_ms < sleep_ms}
+
+
 def torch_bf16_context(steps):
     """The page's comparison column: torch bf16 matmul, 1 x 2560 by 2560 x 13824, weights rotated."""
     torch = _torch()
@@ -515,6 +565,57 @@ def gemv_geometry(N, K):
     return B, B * Wb, P
 
 
+def summarize_profile(path, tail=400):
+    """Print, for every rocpd database under path: per kernel, the dispatches and their
+    durations (ns: mean, median, p10, p90, min) and the median start-to-start period; the same
+    for the last `tail` dispatches of each kernel with at least 2 * tail of them (the dispatch
+    probe's back-to-back launches, when that section ran last); and per kernel and counter, the
+    mean and median value per dispatch and the five largest (the calibration copies are the
+    largest dispatches of the runtime's copy kernel)."""
+    import glob
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(path, "**", "*.db"), recursive=True))
+    if not dbs:
+        print(f"no rocpd database under {path}", file=sys.stderr)
+        sys.exit(1)
+
+    def stats(ev):
+        d = sorted(e - b for b, e in ev)
+        per = sorted(ev[i + 1][0] - ev[i][0] for i in range(len(ev) - 1)) or [0]
+        k = len(d)
+        return (f"{k} | {statistics.mean(d):.1f} | {d[k // 2]} | {d[k // 10]} | {d[9 * k // 10]} | "
+                f"{d[0]} | {per[len(per) // 2]}")
+
+    for dbp in dbs:
+        db = sqlite3.connect(dbp)
+        cur = db.cursor()
+        print(f"# database {os.path.relpath(dbp, path)}")
+        by = {}
+        for name, b, e in cur.execute("select name, start, end from kernels order by start"):
+            by.setdefault(name, []).append((b, e))
+        print("## kernel | dispatches | mean ns | median | p10 | p90 | min | median period")
+        for name, ev in sorted(by.items(), key=lambda kv: -sum(e - b for b, e in kv[1])):
+            print(f"{name[:160]} | {stats(ev)}")
+        for name, ev in by.items():
+            if len(ev) >= 2 * tail:
+                print(f"## last {tail} dispatches: {name[:160]} | {stats(ev[-tail:])}")
+        try:
+            rows = list(cur.execute(
+                "select kernel_name, counter_name, value from counters_collection"))
+        except sqlite3.Error:
+            rows = []
+        if rows:
+            agg = {}
+            for kn, cn, v in rows:
+                agg.setdefault((kn, cn), []).append(v)
+            print("## kernel | counter | dispatches | mean per dispatch | median | largest five")
+            for (kn, cn), vs in sorted(agg.items()):
+                vs.sort()
+                top = ", ".join(f"{v:.1f}" for v in vs[-5:][::-1])
+                print(f"{kn[:160]} | {cn} | {len(vs)} | {statistics.mean(vs):.3f} | "
+                      f"{vs[len(vs) // 2]:.3f} | {top}")
+
+
 ALL_SECTIONS = "fused,layer_set,large,lut,batched,prefill,decode_step,chained_step,ternarize,torch"
 
 
@@ -530,7 +631,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--pmc-calibrate", action="store_true",
                     help="also run a plain copy of 256 MiB (for counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="summarise the rocprofv3 databases (*.db) under DIR and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profile(args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the layer is not sharded across GPUs in this build)", file=sys.stderr)
@@ -550,10 +656,20 @@ def main():
     gbs = nbytes / (ms * 1e-3) / 1e9
     detail = {}
     if args.pmc_calibrate:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        # five plain device-to-device copies of 256 MiB through the HIP runtime (its blit
+        # kernel): a copy of known size for scaling the memory-traffic counters
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_int, ctypes.c_void_p]
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         for _ in range(5):
-            dst.copy_(src)
+            rc = hip.hipMemcpyAsync(dst.data_ptr(), src.data_ptr(), 256 << 20, 3,   # device to device
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"hipMemcpyAsync failed: {rc}")
         torch.cuda.synchronize()
         detail["calibration_copy_bytes"] = 256 << 20
     sections = set() if args.quick else set(args.sections.split(","))
@@ -578,6 +694,8 @@ def main():
         detail["ternarize_pack_bf16_13824x2560"] = ternarize(bl, min(args.steps, 50), 5)
     if "torch" in sections:
         detail["torch_bf16_matmul_13824x2560"] = torch_bf16_context(min(args.steps, 200))
+    if "dispatch_probe" in sections:       # last: its launches are the GEMV kernel's last n
+        detail["dispatch_probe_13824x2560"] = dispatch_probe(bl)
 
     traffic = pmc_traffic()
     B, W, P = gemv_geometry(c.N, c.K)
