@@ -25,11 +25,15 @@
 //   * the activation row is staged once per workgroup in LDS (zero-padded to
 //     Wb*P steps; steps past the band's end re-read its last tile and meet
 //     zero activations), read back as one 16-byte LDS load per step;
-//   * decoding keeps the unsigned codes c = w + 2 and never shifts them into
-//     place: field i of a word is masked in place (factor 4^i, i < 3) and
-//     dotted with activation word i into one of three accumulators; field 3
-//     is shifted down once.  acc = a1 + a4/4 + a16/16 - 2 * sum(x), the last
-//     term removing the +2 offset (padding code 0 contributes nothing);
+//   * decoding keeps the unsigned codes c = w + 2 and removes the +2 offset
+//     once, as -2 * sum(x) (padding code 0 contributes nothing).  int8 rows
+//     are staged split into nibbles (nibble_split), and a word masked two
+//     ways (0x33333333, and after a shift by 2) feeds one unsigned v_dot8 for
+//     the low nibbles and one signed v_dot8 for the high ones per mask: 7
+//     VALU per word.  Rows quantised in the kernel (bf16 input) are staged
+//     whole: field i of a word is masked in place (factor 4^i, i < 3) and
+//     dotted with activation word i by v_dot4 into one of three accumulators,
+//     field 3 shifted down once (9 VALU per word);
 //   * the 16 lanes sharing four rows add their partial sums with DPP row
 //     operations; the Wb wavefronts of a band are added through LDS;
 //   * the fused bf16 path quantises in the workgroup: absmax by DPP within
@@ -135,13 +139,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
         for (int c = 0; c < kCached; ++c) {
             const int idx = tid + c * nthreads;
             if (idx < n_in) {
-                act[idx] = make_int4(xv[c].x, xv[c].y, xv[c].z, xv[c].w);
+                act[idx] = nibble_split(make_int4(xv[c].x, xv[c].y, xv[c].z, xv[c].w));
                 xs = sum_i8x4(xv[c].x, sum_i8x4(xv[c].y, sum_i8x4(xv[c].z, sum_i8x4(xv[c].w, xs))));
             }
         }
         for (int idx = tid + kCached * nthreads; idx < n_in; idx += nthreads) {
             const uint4 v = x16[idx];
-            act[idx] = make_int4(v.x, v.y, v.z, v.w);
+            act[idx] = nibble_split(make_int4(v.x, v.y, v.z, v.w));
             xs = sum_i8x4(v.x, sum_i8x4(v.y, sum_i8x4(v.z, sum_i8x4(v.w, xs))));
         }
     } else {
@@ -194,16 +198,28 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
         asm volatile("" : "+v"(cs), "+v"(offset));
     }
 
-    // 3. P steps of 4 rows x 16 K per lane.
-    RowAcc r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.a1[i] = r.a4[i] = r.a16[i] = 0;
+    // 3. P steps of 4 rows x 16 K per lane: int8 rows were staged split into
+    //    nibbles for v_dot8 (7 VALU per packed word), quantised bf16 rows
+    //    whole for v_dot4 (9).
     const int kc = lane & 15;
-#pragma unroll
-    for (int u = 0; u < P; ++u) dot_slot(w[u], act[(s0 + u) * 16 + kc], r);
     int v[4];
+    if constexpr (!FUSED) {
+        NibAcc r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = r.a1[i] + (r.a4[i] >> 2) + (r.a16[i] >> 4);   // exact
+        for (int i = 0; i < 4; ++i) r.lo[i] = 0, r.hi[i] = 0;
+#pragma unroll
+        for (int u = 0; u < P; ++u) dot_slot_nib(w[u], act[(s0 + u) * 16 + kc], r);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = static_cast<int>(r.lo[i]) + 16 * r.hi[i];   // exact
+    } else {
+        RowAcc r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.a1[i] = r.a4[i] = r.a16[i] = 0;
+#pragma unroll
+        for (int u = 0; u < P; ++u) dot_slot(w[u], act[(s0 + u) * 16 + kc], r);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = r.a1[i] + (r.a4[i] >> 2) + (r.a16[i] >> 4);   // exact
+    }
     // lane l now holds row 4*(l/16) + l%4 of its band (replicated over l/4 % 4)
     const int rsum = row_group_reduce(v, lane);
     if (own) {

@@ -34,6 +34,52 @@ __device__ __forceinline__ void dot_slot(const v4u& wv, const int4& x, RowAcc& r
     dot_word(wv.w, x, r.a1[3], r.a4[3], r.a16[3]);
 }
 
+// The same sums by v_dot8 on 4-bit lanes.  Masked with 0x33333333, a packed
+// word keeps fields 0 and 2 in the low bits of its nibbles: nibble k holds the
+// code (0..3) of element k / 2 for even k and of element 8 + k / 2 for odd k
+// (element e sits at bit 8 (e % 4) + 2 (e / 4)); shifted down by 2 first, it
+// keeps fields 1 and 3, elements 4 + k / 2 and 12 + k / 2.  An int8 activation
+// is 16 h + l with l its low nibble (0..15) and h its high nibble as a signed
+// 4-bit number (-8..7), so sum c x = sum c l + 16 sum c h: one unsigned and
+// one signed v_dot8 per masked word and activation order, 7 VALU per packed
+// word against 9 for the four v_dot4 of dot_word.
+struct NibAcc {
+    uint32_t lo[4];
+    int hi[4];
+};
+
+// A 16-byte activation chunk rearranged for dot_word_nib: the low nibbles of
+// elements 0, 8, 1, 9, 2, 10, 3, 11, their high nibbles, then the same for
+// elements 4, 12, 5, 13, 6, 14, 7, 15 (dwords 0 / 2 of the chunk hold elements
+// 0..3 / 8..11, dwords 1 / 3 elements 4..7 / 12..15).
+__device__ __forceinline__ int4 nibble_split(const int4& x) {
+    constexpr uint32_t kLo = 0x0F0F0F0Fu;
+    const uint32_t x0 = x.x, x1 = x.y, x2 = x.z, x3 = x.w;
+    int4 r;
+    r.x = static_cast<int>((x0 & kLo) | ((x2 << 4) & ~kLo));
+    r.y = static_cast<int>(((x0 >> 4) & kLo) | (x2 & ~kLo));
+    r.z = static_cast<int>((x1 & kLo) | ((x3 << 4) & ~kLo));
+    r.w = static_cast<int>(((x1 >> 4) & kLo) | (x3 & ~kLo));
+    return r;
+}
+
+__device__ __forceinline__ void dot_word_nib(uint32_t w, const int4& xn, uint32_t& lo, int& hi) {
+    const uint32_t a = w & 0x33333333u;
+    const uint32_t b = (w >> 2) & 0x33333333u;
+    lo = __builtin_amdgcn_udot8(a, static_cast<uint32_t>(xn.x), lo, false);
+    hi = __builtin_amdgcn_sdot8(static_cast<int>(a), xn.y, hi, false);
+    lo = __builtin_amdgcn_udot8(b, static_cast<uint32_t>(xn.z), lo, false);
+    hi = __builtin_amdgcn_sdot8(static_cast<int>(b), xn.w, hi, false);
+}
+
+// One K step of a lane on a chunk split by nibble_split.
+__device__ __forceinline__ void dot_slot_nib(const v4u& wv, const int4& xn, NibAcc& r) {
+    dot_word_nib(wv.x, xn, r.lo[0], r.hi[0]);
+    dot_word_nib(wv.y, xn, r.lo[1], r.hi[1]);
+    dot_word_nib(wv.z, xn, r.lo[2], r.hi[2]);
+    dot_word_nib(wv.w, xn, r.lo[3], r.hi[3]);
+}
+
 // Ptr: const v4u*, or a pointer into the global address space (kernels that
 // read their pointers from memory rather than kernel arguments cast them, so
 // that the loads are global rather than flat loads).
