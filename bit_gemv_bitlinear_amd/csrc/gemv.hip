@@ -55,14 +55,14 @@ namespace bl {
 
 namespace {
 
-// C = 16-byte activation chunks per thread loaded ahead of the weights and
-// kept in registers (1, 2 or 4, a template argument chosen per shape).
-// Chunks beyond them are loaded after the weights, and since the waits count
-// loads in issue order, using them waits for every weight; so C covers the
-// row wherever it can (bf16 rows have twice the chunks of int8 rows: 2560 x
-// 2 B over 128 threads for qkv and o, 6912 x 2 B over 256 threads for down).
-// Chunks a thread does not need cost code on the path to the main loop, so C
-// is no larger than the row needs.
+// C = 16-element activation chunks per thread (16 bytes of int8, 32 of bf16)
+// loaded ahead of the weights and kept in registers (1, 2 or 4, a template
+// argument chosen per shape).  Chunks beyond them are loaded after the
+// weights, and since the waits count loads in issue order, using them waits
+// for every weight; so C covers the row wherever it can (2560 / 16 = 160
+// chunks over 128 threads for qkv and o, 6912 / 16 = 432 over 256 threads
+// for down).  Chunks a thread does not need cost code on the path to the
+// main loop, so C is no larger than the row needs.
 //
 // Row n's weight scale is ws[n / seg], seg = N / ws_num, found as
 // (n * seg_mul) >> seg_shift (see seg_divisor()).  B bands per workgroup, 2^lw
@@ -112,15 +112,26 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
     const uint32_t n_ws = static_cast<uint32_t>(min(n_out, N - 1));
     // unconditional: no branch, no early wait
     const uint16_t wsb = ws[(static_cast<uint64_t>(n_ws) * seg_mul) >> seg_shift];
+    // C 16-element chunks of the row per thread: 16 bytes of int8, or 32
+    // bytes (two adjacent 16-byte loads) of bf16, so that a thread quantises
+    // whole chunks and can stage them split into nibbles.
     constexpr int kCached = C;
-    uint4 xv[kCached];
-    const int n_in = FUSED ? (K >> 3) : n16;   // 16-byte input chunks
+    constexpr int kLoads = FUSED ? 2 * C : C;
+    uint4 xv[kLoads];
     const uint4* x16 = reinterpret_cast<const uint4*>(xin);
 #pragma unroll
     for (int c = 0; c < kCached; ++c) {
-        const int idx = tid + c * nthreads;
-        xv[c] = make_uint4(0, 0, 0, 0);
-        if (idx < n_in) xv[c] = x16[idx];
+        const int q = tid + c * nthreads;
+        if constexpr (FUSED) {
+            xv[2 * c] = xv[2 * c + 1] = make_uint4(0, 0, 0, 0);
+            if (q < n16) {
+                xv[2 * c] = x16[2 * q];
+                xv[2 * c + 1] = x16[2 * q + 1];
+            }
+        } else {
+            xv[c] = make_uint4(0, 0, 0, 0);
+            if (q < n16) xv[c] = x16[q];
+        }
     }
     const v4u* tiles = packed + static_cast<size_t>(band) * S * 64 + lane;
     v4u w[P];
@@ -138,12 +149,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
 #pragma unroll
         for (int c = 0; c < kCached; ++c) {
             const int idx = tid + c * nthreads;
-            if (idx < n_in) {
+            if (idx < n16) {
                 act[idx] = nibble_split(make_int4(xv[c].x, xv[c].y, xv[c].z, xv[c].w));
                 xs = sum_i8x4(xv[c].x, sum_i8x4(xv[c].y, sum_i8x4(xv[c].z, sum_i8x4(xv[c].w, xs))));
             }
         }
-        for (int idx = tid + kCached * nthreads; idx < n_in; idx += nthreads) {
+        for (int idx = tid + kCached * nthreads; idx < n16; idx += nthreads) {
             const uint4 v = x16[idx];
             act[idx] = nibble_split(make_int4(v.x, v.y, v.z, v.w));
             xs = sum_i8x4(v.x, sum_i8x4(v.y, sum_i8x4(v.z, sum_i8x4(v.w, xs))));
@@ -152,33 +163,31 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
         float amax = 0.0f;
 #pragma unroll
         for (int c = 0; c < kCached; ++c)
-            if (tid + c * nthreads < n_in) amax = absmax8_bf16(xv[c], amax);
-        for (int idx = tid + kCached * nthreads; idx < n_in; idx += nthreads)
-            amax = absmax8_bf16(x16[idx], amax);
+            if (tid + c * nthreads < n16)
+                amax = absmax8_bf16(xv[2 * c], absmax8_bf16(xv[2 * c + 1], amax));
+        for (int q = tid + kCached * nthreads; q < n16; q += nthreads)
+            amax = absmax8_bf16(x16[2 * q], absmax8_bf16(x16[2 * q + 1], amax));
         amax = wave_max(amax);
         if (lane == 0) amax_sh[wave] = amax;
         __syncthreads();
         amax = amax_sh[0];
         for (int i = 1; i < W; ++i) amax = fmaxf(amax, amax_sh[i]);
         sm = 127.0f / fmaxf(amax, 1e-5f);
-        uint2* act8 = reinterpret_cast<uint2*>(act);
         const bool write_q = (blockIdx.x == 0) && (q_out != nullptr);
+        // quantise a whole chunk (two 8-element halves), stage it split
+        auto put = [&](int q, const uint4& lo, const uint4& hi) {
+            const uint2 o0 = quant8_bf16(lo, sm), o1 = quant8_bf16(hi, sm);
+            const int4 ch = make_int4(o0.x, o0.y, o1.x, o1.y);
+            act[q] = nibble_split(ch);
+            xs = sum_i8x4(o0.x, sum_i8x4(o0.y, sum_i8x4(o1.x, sum_i8x4(o1.y, xs))));
+            if (write_q) reinterpret_cast<int4*>(q_out)[q] = ch;
+        };
 #pragma unroll
         for (int c = 0; c < kCached; ++c) {
-            const int idx = tid + c * nthreads;
-            if (idx < n_in) {
-                const uint2 o = quant8_bf16(xv[c], sm);
-                act8[idx] = o;
-                xs = sum_i8x4(o.x, sum_i8x4(o.y, xs));
-                if (write_q) reinterpret_cast<uint2*>(q_out)[idx] = o;
-            }
+            const int q = tid + c * nthreads;
+            if (q < n16) put(q, xv[2 * c], xv[2 * c + 1]);
         }
-        for (int idx = tid + kCached * nthreads; idx < n_in; idx += nthreads) {
-            const uint2 o = quant8_bf16(x16[idx], sm);
-            act8[idx] = o;
-            xs = sum_i8x4(o.x, sum_i8x4(o.y, xs));
-            if (write_q) reinterpret_cast<uint2*>(q_out)[idx] = o;
-        }
+        for (int q = tid + kCached * nthreads; q < n16; q += nthreads) put(q, x16[2 * q], x16[2 * q + 1]);
         if (blockIdx.x == 0 && s_out != nullptr && tid == 0) s_out[0] = sm;
     }
     for (int i = n16 + tid; i < padded16; i += nthreads) act[i] = make_int4(0, 0, 0, 0);
@@ -198,28 +207,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
         asm volatile("" : "+v"(cs), "+v"(offset));
     }
 
-    // 3. P steps of 4 rows x 16 K per lane: int8 rows were staged split into
-    //    nibbles for v_dot8 (7 VALU per packed word), quantised bf16 rows
-    //    whole for v_dot4 (9).
+    // 3. P steps of 4 rows x 16 K per lane on the chunks staged split into
+    //    nibbles (v_dot8, 7 VALU per packed word).
     const int kc = lane & 15;
+    NibAcc r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.lo[i] = 0, r.hi[i] = 0;
+#pragma unroll
+    for (int u = 0; u < P; ++u) dot_slot_nib(w[u], act[(s0 + u) * 16 + kc], r);
     int v[4];
-    if constexpr (!FUSED) {
-        NibAcc r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.lo[i] = 0, r.hi[i] = 0;
-#pragma unroll
-        for (int u = 0; u < P; ++u) dot_slot_nib(w[u], act[(s0 + u) * 16 + kc], r);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = static_cast<int>(r.lo[i]) + 16 * r.hi[i];   // exact
-    } else {
-        RowAcc r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r.a1[i] = r.a4[i] = r.a16[i] = 0;
-#pragma unroll
-        for (int u = 0; u < P; ++u) dot_slot(w[u], act[(s0 + u) * 16 + kc], r);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = r.a1[i] + (r.a4[i] >> 2) + (r.a16[i] >> 4);   // exact
-    }
+    for (int i = 0; i < 4; ++i) v[i] = static_cast<int>(r.lo[i]) + 16 * r.hi[i];   // exact
     // lane l now holds row 4*(l/16) + l%4 of its band (replicated over l/4 % 4)
     const int rsum = row_group_reduce(v, lane);
     if (own) {
@@ -267,9 +265,11 @@ const std::array<std::array<KernelRow, 3>, 2> kKernels = {{
     {{kernel_table<false, 1, false>(std::make_integer_sequence<int, kMaxSteps>{}),
       kernel_table<false, 2, false>(std::make_integer_sequence<int, kMaxSteps>{}),
       kernel_table<false, 4, false>(std::make_integer_sequence<int, kMaxSteps>{})}},
+    // bf16 rows: at most 2 chunks (4 loads) per thread, the registers of
+    // 4 int8 chunks; longer rows load the rest in the staging loop
     {{kernel_table<true, 1, false>(std::make_integer_sequence<int, kMaxSteps>{}),
       kernel_table<true, 2, false>(std::make_integer_sequence<int, kMaxSteps>{}),
-      kernel_table<true, 4, false>(std::make_integer_sequence<int, kMaxSteps>{})}},
+      kernel_table<true, 2, false>(std::make_integer_sequence<int, kMaxSteps>{})}},
 }};
 // int8 input with one wavefront per band: [log2 C][P - 1]
 const std::array<KernelRow, 3> kKernelsOwn = {{
@@ -290,7 +290,7 @@ hipError_t launch(bool fused, const void* x, const uint8_t* packed, const float*
     while ((1 << lw) < wb) ++lw;
     const size_t lds = static_cast<size_t>(wb) * g.steps * kTileK;
     // chunks of the activation row per thread, rounded up to 1, 2 or 4
-    const int chunks = fused ? K / 8 : K / 16;
+    const int chunks = K / 16;          // 16-element chunks (32 bytes of bf16)
     const int threads = g.waves * 64;
     const int need = (chunks + threads - 1) / threads;
     const int lc = need <= 1 ? 0 : need <= 2 ? 1 : 2;
