@@ -31,8 +31,9 @@
 //     K <= 10240) is a template argument of the body, chosen per workgroup
 //     by a uniform branch, so that the compiler counts every chunk's loads
 //     exactly in its waits;
-//   * dot products, row reduction and epilogue are those of the single GEMV
-//     (gemv_core.hpp, common.hpp); each wavefront writes its own 16 rows.
+//   * dot products (v_dot8 on the row staged split into nibbles), row
+//     reduction and epilogue are those of the single GEMV (gemv_core.hpp,
+//     common.hpp); each wavefront writes its own 16 rows.
 #include <algorithm>
 #include <vector>
 
@@ -45,7 +46,7 @@ namespace {
 
 constexpr int kGroupWaves = 4;          // wavefronts (= bands) per workgroup
 constexpr int kGroupChunk = 10;         // tiles per chunk of a wavefront's band
-constexpr int kGroupCached = 4;         // 16-byte bf16 chunks of the row per thread in registers
+constexpr int kGroupCached = 2;         // 16-element chunks (32 bytes of bf16) per thread in registers
 
 __device__ __forceinline__ uint4 as_uint4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
@@ -69,14 +70,17 @@ __device__ __forceinline__ void group_body(const GroupWork& g, int4* __restrict_
     const int n_out = band_lin * kTileRows + 4 * (lane >> 4) + (lane & 3);
     const uint32_t n_ws = static_cast<uint32_t>(min(n_out, N - 1));
     const uint16_t wsb = global(g.ws)[(static_cast<uint64_t>(n_ws) * g.seg_mul) >> g.seg_shift];
-    const int n_in = K >> 3;            // 16-byte chunks of the bf16 row
+    const int n16 = K >> 4;             // 16-element chunks of the row (32 bytes of bf16)
     const global_ptr<const v4u> x16 = global(reinterpret_cast<const v4u*>(g.x));
-    uint4 xv[C];
+    uint4 xv[2 * C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        const int idx = tid + c * (kGroupWaves * 64);
-        xv[c] = make_uint4(0, 0, 0, 0);
-        if (idx < n_in) xv[c] = as_uint4(x16[idx]);
+        const int q = tid + c * (kGroupWaves * 64);
+        xv[2 * c] = xv[2 * c + 1] = make_uint4(0, 0, 0, 0);
+        if (q < n16) {
+            xv[2 * c] = as_uint4(x16[2 * q]);
+            xv[2 * c + 1] = as_uint4(x16[2 * q + 1]);
+        }
     }
     const global_ptr<const v4u> tiles =
         global(reinterpret_cast<const v4u*>(g.packed)) + static_cast<size_t>(band) * S * 64 + lane;
@@ -86,36 +90,35 @@ __device__ __forceinline__ void group_body(const GroupWork& g, int4* __restrict_
     // Nothing above this point: a wait for the row must not hold back a weight load.
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. Quantise the row into LDS ([W2A8] §六 item 3) and sum it (for the
-    //    +2 code offset).
+    // 2. Quantise the row into LDS ([W2A8] §六 item 3), whole 16-element
+    //    chunks staged split into nibbles for v_dot8, and sum it (for the +2
+    //    code offset).
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < C; ++c)
-        if (tid + c * (kGroupWaves * 64) < n_in) amax = absmax8_bf16(xv[c], amax);
-    for (int idx = tid + C * (kGroupWaves * 64); idx < n_in; idx += kGroupWaves * 64)
-        amax = absmax8_bf16(as_uint4(x16[idx]), amax);
+        if (tid + c * (kGroupWaves * 64) < n16)
+            amax = absmax8_bf16(xv[2 * c], absmax8_bf16(xv[2 * c + 1], amax));
+    for (int q = tid + C * (kGroupWaves * 64); q < n16; q += kGroupWaves * 64)
+        amax = absmax8_bf16(as_uint4(x16[2 * q]), absmax8_bf16(as_uint4(x16[2 * q + 1]), amax));
     amax = wave_max(amax);
     if (lane == 0) amax_sh[wave] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(amax_sh[0], amax_sh[1]), fmaxf(amax_sh[2], amax_sh[3]));
     const float sm = 127.0f / fmaxf(amax, 1e-5f);
-    uint2* act8 = reinterpret_cast<uint2*>(act);
     int xs = 0;
+    auto put = [&](int q, const uint4& lo, const uint4& hi) {
+        const uint2 o0 = quant8_bf16(lo, sm), o1 = quant8_bf16(hi, sm);
+        act[q] = nibble_split(make_int4(o0.x, o0.y, o1.x, o1.y));
+        xs = sum_i8x4(o0.x, sum_i8x4(o0.y, sum_i8x4(o1.x, sum_i8x4(o1.y, xs))));
+    };
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        const int idx = tid + c * (kGroupWaves * 64);
-        if (idx < n_in) {
-            const uint2 o = quant8_bf16(xv[c], sm);
-            act8[idx] = o;
-            xs = sum_i8x4(o.x, sum_i8x4(o.y, xs));
-        }
+        const int q = tid + c * (kGroupWaves * 64);
+        if (q < n16) put(q, xv[2 * c], xv[2 * c + 1]);
     }
-    for (int idx = tid + C * (kGroupWaves * 64); idx < n_in; idx += kGroupWaves * 64) {
-        const uint2 o = quant8_bf16(as_uint4(x16[idx]), sm);
-        act8[idx] = o;
-        xs = sum_i8x4(o.x, sum_i8x4(o.y, xs));
-    }
-    for (int i = (K >> 4) + tid; i < NCH * P * 16; i += kGroupWaves * 64) act[i] = make_int4(0, 0, 0, 0);
+    for (int q = tid + C * (kGroupWaves * 64); q < n16; q += kGroupWaves * 64)
+        put(q, as_uint4(x16[2 * q]), as_uint4(x16[2 * q + 1]));
+    for (int i = n16 + tid; i < NCH * P * 16; i += kGroupWaves * 64) act[i] = make_int4(0, 0, 0, 0);
     xs = wave_sum(xs);
     if (lane == 0) xsum_sh[wave] = xs;
     __syncthreads();
@@ -124,14 +127,14 @@ __device__ __forceinline__ void group_body(const GroupWork& g, int4* __restrict_
 
     // 3. NCH chunks of P steps of 4 rows x 16 K per lane; chunk c + 2 goes
     //    out as soon as chunk c is dotted, so two chunks stay in flight.
-    RowAcc r;
+    NibAcc r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.a1[i] = r.a4[i] = r.a16[i] = 0;
+    for (int i = 0; i < 4; ++i) r.lo[i] = 0, r.hi[i] = 0;
     const int kc = lane & 15;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-        for (int u = 0; u < P; ++u) dot_slot(w[c & 1][u], act[(c * P + u) * 16 + kc], r);
+        for (int u = 0; u < P; ++u) dot_slot_nib(w[c & 1][u], act[(c * P + u) * 16 + kc], r);
         if (c + 2 < NCH) {
             // not above the dot products: the chunk's registers would then
             // need a third buffer (252 instead of ~130 VGPRs at three chunks)
@@ -141,7 +144,7 @@ __device__ __forceinline__ void group_body(const GroupWork& g, int4* __restrict_
     }
     int v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = r.a1[i] + (r.a4[i] >> 2) + (r.a16[i] >> 4);   // exact
+    for (int i = 0; i < 4; ++i) v[i] = static_cast<int>(r.lo[i]) + 16 * r.hi[i];   // exact
     const int rsum = row_group_reduce(v, lane);
 
     // 4. Lane l with (l / 4) % 4 == 0 holds row 4 * (l / 16) + l % 4 of the band.
