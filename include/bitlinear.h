@@ -191,8 +191,9 @@ int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int 
  * The activation scale divides: s = 127/amax quantised the activations, so
  * y approximates x . w^T * ws.
  * M == 1 with K <= 61440 runs the GEMV kernel (workgroups of 1, 2 or 4
- * 16-row bands, v_dot4 on masked codes).  2 <= M <= 32 with K <= 2560 (a
- * few sequences decoded together) runs the band kernel: int8 MFMA
+ * 16-row bands, v_dot8 on masked codes and nibble-split activations).
+ * 2 <= M <= 32 with K <= 2560 (a few sequences decoded together) runs the
+ * band kernel: int8 MFMA
  * (v_mfma_i32_16x16x64_i8), one wavefront per 16 weight rows over all of K,
  * the activation rows staged once per workgroup in LDS.  M >= 65 with
  * N >= 8192 (prompt processing on wide layers, the prompt lengths of
