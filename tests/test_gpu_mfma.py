@@ -83,10 +83,13 @@ def test_extremes_and_segments(bl):
     check(bl, "extremes_ws4", w, xq, s, synth.ws_bits(g, 4), 4)
 
 
-def test_bf16_entry_with_staging(bl):
+@pytest.mark.parametrize("M,N", [(48, 640), (16, 1000), (32, 13824)])
+def test_bf16_entry_with_staging(bl, M, N):
+    # the bf16 entry quantises into q_out / s_out, then runs the layer kernel
+    # for M >= 2: the band kernel for M = 16, 32, the streaming kernel for 48
     import torch
-    M, N, K = 48, 640, 2560
-    c = synth.make_float_gemv("bf16_m48", M, N, K, 2, 2718, bf16=True)
+    K = 2560
+    c = synth.make_float_gemv(f"bf16_m{M}", M, N, K, 2, 2718 + M, bf16=True)
     print(f"mfma bf16 entry M={M}", flush=True)
     packed = bl.pack_ternary_weights(dev(c.w))
     q = torch.empty((M, K), dtype=torch.int8, device="cuda")
