@@ -37,31 +37,28 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round an fp64 value to bf16, ties to even, straight from the fp64 bits (no
-// intermediate fp32 rounding, so there is no double rounding).  A bf16 value
-// is r * 2^q with q = E - 7 for |v| >= 2^-126 (E = exponent of the leading
-// bit) and q = -133 below; its encoding is ((q + 133) << 7) + r, which also
-// carries correctly into the exponent when rounding reaches the next binade.
-__device__ __forceinline__ uint16_t bf16_from_double_rne(double v) {
-    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
-    const uint32_t sign = static_cast<uint32_t>(b >> 48) & 0x8000u;
-    const uint64_t mag = b & 0x7FFFFFFFFFFFFFFFull;
-    if (mag > 0x7FF0000000000000ull) return static_cast<uint16_t>(sign | 0x7FC0u);   // NaN
-    if (mag >= 0x7FF0000000000000ull) return static_cast<uint16_t>(sign | 0x7F80u);  // inf
-    const int exp = static_cast<int>(mag >> 52);
-    if (exp == 0) return static_cast<uint16_t>(sign);   // |v| < 2^-1022 rounds to zero
-    const int E = exp - 1023;
-    const uint64_t m = (mag & ((1ull << 52) - 1)) | (1ull << 52);   // v = m * 2^(E-52)
-    const int q = (E >= -126) ? (E - 7) : -133;
-    const int shift = q - (E - 52);                                  // >= 45
-    if (shift > 54) return static_cast<uint16_t>(sign);             // below half of 2^-133
-    uint64_t r = m >> shift;
-    const uint64_t rem = m & ((1ull << shift) - 1);
-    const uint64_t half = 1ull << (shift - 1);
-    if (rem > half || (rem == half && (r & 1))) ++r;
-    int64_t bits = (static_cast<int64_t>(q + 133) << 7) + static_cast<int64_t>(r);
-    if (bits >= 0x7F80) bits = 0x7F80;
-    return static_cast<uint16_t>(sign | static_cast<uint32_t>(bits));
+// bf16 rounding (nearest, ties to even) of an fp64 value in two hardware
+// steps: to fp32 rounded to odd, then fp32 to bf16 with ties to even.  An
+// intermediate format with at least two more significant bits than the
+// target makes that pair equal to one direct rounding (Boldo and Melquiond,
+// "Emulation of FMA and correctly rounded sums: proved algorithms using
+// rounding to odd", IEEE Trans. Computers 57(4), 2008); fp32 carries 24 bits
+// against bf16's 8, also among the subnormals (quantum 2^-149 against
+// 2^-133), and shares bf16's exponent range, so a value beyond it lands on
+// fp32's largest finite value, which rounds on to infinity as it should.
+// Rounding to odd: the nearest fp32 (the conversion's own rounding, ties to
+// even, with fp32 subnormals kept), and when that is inexact and even, its
+// neighbour on the other side of the value, which is odd.  NaN gives the
+// quiet NaN 0x7FC0.  About ten instructions, no 64-bit shifts: the exact
+// paths of the epilogues below are short, which matters because they run
+// rarely and their code is cold.
+__device__ __forceinline__ uint32_t bf16_rne_f64(double d) {
+    const float f = static_cast<float>(d);
+    uint32_t u = __float_as_uint(f);
+    const double back = static_cast<double>(f);
+    if (back != d && !(u & 1u)) u += fabs(back) > fabs(d) ? 0xFFFFFFFFu : 1u;
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return d != d ? 0x7FC0u : u;
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -80,7 +77,7 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 // the quotient is rounded once to fp64, then once to bf16.
 __device__ __forceinline__ uint16_t epilogue_bf16(int32_t acc, float ws, float s) {
     const double v = (static_cast<double>(acc) * static_cast<double>(ws)) / static_cast<double>(s);
-    return bf16_from_double_rne(v);
+    return static_cast<uint16_t>(bf16_rne_f64(v));
 }
 
 // The same value as epilogue_bf16 without a division on the common path.

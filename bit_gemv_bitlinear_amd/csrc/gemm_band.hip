@@ -1,6 +1,6 @@
 // gemm_band.hip -- the batched W2A8 ternary layer for a few rows of
-// activations (2 <= M <= 32, K <= 2560) on gfx950 int8 MFMA, one wavefront
-// per 16-row band of weights.
+// activations (2 <= M <= 64, K <= 2560) on gfx950 int8 MFMA, one wavefront
+// per one or two 16-row bands of weights.
 //
 // Source page: "BitNet GPU 推理框架：从零构建 W2A8 的 2-bit 大模型 CUDA GEMV 内核"
 // (blog.gitcode.com), cited as [W2A8]: §5.2 (codes w + 2, interleaved words),
@@ -10,10 +10,16 @@
 // contraction.
 //
 // Mapping (this library's design):
-//   * a workgroup is 4 wavefronts over 4 consecutive 16-row bands (64 output
-//     rows n) and all M rows of activations (MT tiles of 16); each wavefront
-//     owns one band over the whole of K, so no partial sums cross
-//     wavefronts and the epilogue runs from the MFMA accumulators;
+//   * a workgroup is 4 wavefronts over 4 BW consecutive 16-row bands (64 BW
+//     output rows n) and a group of up to 16 MT rows of activations (MT
+//     tiles of 16); each wavefront owns BW bands over the whole of K, so no
+//     partial sums cross wavefronts and the epilogue runs from the MFMA
+//     accumulators.  BW = 1 with one group of all M <= 32 rows; BW = 2 with
+//     groups of 32 rows for M = 33 .. 64, where all rows of K = 2560 would
+//     not fit the LDS: a wavefront then reads each staged operand once for
+//     two bands' MFMAs, so a CU reads no more LDS per tile than at M = 32,
+//     and the row groups of one band group run on one XCD (workgroup ids 8
+//     apart), which reads those weights through one L2;
 //   * the wavefront's P weight tiles (1 KiB each) are loaded exactly as the
 //     GEMV loads them -- one coalesced 16-byte load per lane per tile, all
 //     issued up front -- after the activations the workgroup stages;
@@ -52,8 +58,8 @@ namespace bl {
 
 namespace {
 
-constexpr int kBands = 4;                 // 16-row bands (= wavefronts) per workgroup
-constexpr int kThreads = kBands * 64;
+constexpr int kWaves = 4;                 // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;
 constexpr int kRowPad = 16;               // bytes past each staged activation row
 constexpr int kRawBufferFlags = 0x00020000;   // word 3 of a buffer descriptor: 32-bit data format
 constexpr int kOutOfRange = 0x7FFFFFF0;       // a buffer offset past any record: reads as zero
@@ -74,15 +80,41 @@ __device__ __forceinline__ int field(uint32_t w) {
     return static_cast<int>(w & (0x03030303u << (2 * F)));
 }
 
-// MT = m tiles of 16 rows (M <= 16 MT); P = 256-K tiles per band (= ceil(K / 256)).
-// One wavefront per band.  (Two per band, each dotting half the tiles and
+// Workgroup id -> (band group bg, row group mg), H row groups.  The GPU hands
+// workgroups to its eight XCDs in turn (id mod 8); the H row groups of a band
+// group get ids 8 apart, on one XCD, so that they read its weights through
+// one L2.  With H = 1 the id is the band group.
+template <int H>
+__device__ __forceinline__ void split_group_id(int id, int groups, int& bg, int& mg) {
+    static_assert(H == 1 || H == 2, "one or two row groups");
+    if constexpr (H == 1) {
+        bg = id;
+        mg = 0;
+    } else {
+        const int full = groups >> 3;              // runs of 8 band groups
+        const int run = id >> 4;
+        if (run < full) {
+            mg = (id >> 3) & 1;
+            bg = 8 * run + (id & 7);
+        } else {
+            const int r = id - 16 * full;
+            const int rest = groups - 8 * full;    // 1 .. 7 band groups left
+            mg = r >= rest ? 1 : 0;
+            bg = 8 * full + r - mg * rest;
+        }
+    }
+}
+
+// MT = m tiles of 16 rows per row group; P = 256-K tiles per band (= ceil(K / 256));
+// BW = bands per wavefront.  BW = 1: one row group (M <= 16 MT); BW = 2: two
+// row groups of 16 MT rows (M = 33 .. 64 with MT = 2).  (Two per band, each dotting half the tiles and
 // handing its sums to the other through LDS, measured slower at 13824 x 2560:
 // M = 16 4.76 -> 5.07 us, M = 32 5.91 -> 6.46 us, with an earlier decode.
 // Four more wavefronts that only stage the activations, so that the bands'
 // weight loads go out at once, measured slower still -- M = 16 4.44 -> 5.37
 // us: a CU returns its loads in the order they were issued, so the rows
 // then arrive behind the weights.)
-template <int MT, int P>
+template <int MT, int P, int BW>
 __global__ __launch_bounds__(kThreads) void gemm_band_kernel(
     const int8_t* __restrict__ xq, const v4u* __restrict__ packed, const float* __restrict__ s,
     const uint16_t* __restrict__ ws, uint32_t seg_mul, int seg_shift, uint16_t* __restrict__ y,
@@ -93,6 +125,8 @@ __global__ __launch_bounds__(kThreads) void gemm_band_kernel(
     __shared__ int rowsum_sh[16 * MT];
     constexpr int kRows = 16 * MT;
     constexpr int kPitch = P * kTileK + kRowPad;
+    constexpr int kGroupBands = kWaves * BW;
+    constexpr int H = BW;                             // row groups
     // MT = 1: thread t stages chunks t % 16 + 16 i of row t / 16 (one per tile);
     // MT = 2: thread t stages quads t, t + 256, ... (see below).
     constexpr int kQuadsAll = kRows * 4 * P;                       // a multiple of 64
@@ -102,13 +136,21 @@ __global__ __launch_bounds__(kThreads) void gemm_band_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nbands = (N + kTileRows - 1) / kTileRows;
-    const int band_lin = static_cast<int>(blockIdx.x) * kBands + wave;
-    const int band = min(band_lin, nbands - 1);
+    int bg, mg;
+    split_group_id<H>(static_cast<int>(blockIdx.x), (nbands + kGroupBands - 1) / kGroupBands, bg,
+                      mg);
+    const int m0 = mg * kRows;                        // first activation row of the group
     const int j = lane & 15;
     const int g = lane >> 4;
-    const int n = band_lin * kTileRows + j;          // this lane's output column
+    // band b of this wavefront: 16 rows from band_lin[b]; n[b] = this lane's output column
+    int band_lin[BW], n[BW];
+#pragma unroll
+    for (int b = 0; b < BW; ++b) {
+        band_lin[b] = bg * kGroupBands + wave * BW + b;
+        n[b] = band_lin[b] * kTileRows + j;
+    }
 
-    // 1. The row scale and this lane's weight scale, this thread's share of
+    // 1. The row scale and this lane's weight scales, this thread's share of
     //    the activation rows, then every weight tile.  Chunks past K and rows
     //    past M are read at an offset beyond the buffer, which the hardware
     //    returns as zeros without a memory access; there is no branch around
@@ -125,11 +167,15 @@ __global__ __launch_bounds__(kThreads) void gemm_band_kernel(
         const_cast<float*>(s), 0, 4 * M, kRawBufferFlags);
     const int srow = tid & (kRows - 1);            // kRows is 16 or 32
     const float s_row = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(sb, 4 * min(srow, M - 1), 0, 0));
+        float, __builtin_amdgcn_raw_buffer_load_b32(sb, 4 * min(m0 + srow, M - 1), 0, 0));
     // (the index as a 32-bit unsigned: a signed one made the compiler read an
     // undefined high half from a register still being loaded, waiting for it)
-    const uint32_t n_ws = static_cast<uint32_t>(min(n, N - 1));
-    const uint16_t wsb = ws[(static_cast<uint64_t>(n_ws) * seg_mul) >> seg_shift];
+    uint16_t wsb[BW];
+#pragma unroll
+    for (int b = 0; b < BW; ++b) {
+        const uint32_t n_ws = static_cast<uint32_t>(min(n[b], N - 1));
+        wsb[b] = ws[(static_cast<uint64_t>(n_ws) * seg_mul) >> seg_shift];
+    }
     const int nck = K >> 4;                        // real 16-byte chunks per row
     v4u a[kALoads];
     if constexpr (MT == 1) {
@@ -140,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void gemm_band_kernel(
         for (int i = 0; i < P; ++i) {
             const int c = (tid & 15) + 16 * i;
             a[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                xb, c < nck && r < M ? __mul24(r, K) + 16 * c : kOutOfRange, 0, 0);
+                xb, c < nck && m0 + r < M ? __mul24(m0 + r, K) + 16 * c : kOutOfRange, 0, 0);
         }
     } else {
         // Quad (u, g) of a row is its 16-wide K chunks g, g + 4, g + 8,
@@ -156,18 +202,30 @@ __global__ __launch_bounds__(kThreads) void gemm_band_kernel(
             const int ck = 16 * (jq >> 2) + (jq & 3);   // chunk of v = 0
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const bool real = (i + 1 < kIters || q < kQuadsAll) && ck + 4 * v < nck && r < M;
+                const bool real =
+                    (i + 1 < kIters || q < kQuadsAll) && ck + 4 * v < nck && m0 + r < M;
                 a[4 * i + v] = __builtin_amdgcn_raw_buffer_load_b128(
-                    xb, real ? __mul24(r, K) + 16 * (ck + 4 * v) : kOutOfRange, 0, 0);
+                    xb, real ? __mul24(m0 + r, K) + 16 * (ck + 4 * v) : kOutOfRange, 0, 0);
             }
         }
     }
     // The activation loads go out first, so that a wait for them leaves the
     // weight loads in flight.
     __builtin_amdgcn_sched_barrier(0);
-    const v4u* tiles = packed + static_cast<size_t>(band) * P * 64 + lane;
-    v4u wt[P];
-    load_steps_ordered<P>(tiles, 0, P - 1, wt);
+    // Tile u of every band goes out before tile u + 1 of any, in the order
+    // the loop below waits for them.
+    const v4u* tiles[BW];
+#pragma unroll
+    for (int b = 0; b < BW; ++b)
+        tiles[b] = packed + static_cast<size_t>(min(band_lin[b], nbands - 1)) * P * 64 + lane;
+    v4u wt[BW][P];
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+#pragma unroll
+        for (int b = 0; b < BW; ++b) {
+            wt[b][u] = __builtin_nontemporal_load(tiles[b] + u * 64);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     // No load may sink below this point (the compiler would otherwise move the
     // activation loads to their first use, behind a wait that counts every
     // weight load too), and nothing may be scheduled above it.
@@ -232,49 +290,66 @@ __global__ __launch_bounds__(kThreads) void gemm_band_kernel(
     inv_s_sh[srow] = 1.0 / static_cast<double>(s_row);
     __syncthreads();
 
-    // 3. Per tile: through the wavefront's slot, lane (j, g) takes the words of
-    //    row j for chunks g, g + 4, g + 8, g + 12; MFMA f multiplies field f of
-    //    the four (unsigned codes c = w + 2, masked in place) into the
-    //    accumulator of its factor: 1 (fields 0 and 3), 4 (field 1), 16
-    //    (field 2).
+    // 3. Per tile: through the wavefront's slots, lane (j, g) takes the words
+    //    of row j of each band for chunks g, g + 4, g + 8, g + 12; MFMA f
+    //    multiplies field f of the four (unsigned codes c = w + 2, masked in
+    //    place) into the accumulator of its factor: 1 (fields 0 and 3), 4
+    //    (field 1), 16 (field 2).  An activation operand read from LDS serves
+    //    the MFMAs of all BW bands.
     // This lane's rows' constants for the epilogue, read now so that their
     // LDS latency passes under the main loop: the code offset -2 sum(x), the
-    // fp64 scale ws / s and s itself, for rows m = 16 mt + 4 g + v.
-    const float wsf = bf16_to_float(wsb);
+    // fp64 scale ws / s of each band and s itself, for rows m0 + 16 mt + 4 g + v.
+    float wsf[BW];
+#pragma unroll
+    for (int b = 0; b < BW; ++b) wsf[b] = bf16_to_float(wsb[b]);
     int offset[MT][4];
-    double cs[MT][4];
+    double cs[BW][MT][4];
     float sm[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int m = 16 * mt + 4 * g + v;
-            offset[mt][v] = -2 * rowsum_sh[m];
-            cs[mt][v] = static_cast<double>(wsf) * inv_s_sh[m];
-            sm[mt][v] = s_sh[m];
+            const int r = 16 * mt + 4 * g + v;
+            offset[mt][v] = -2 * rowsum_sh[r];
+#pragma unroll
+            for (int b = 0; b < BW; ++b) cs[b][mt][v] = static_cast<double>(wsf[b]) * inv_s_sh[r];
+            sm[mt][v] = s_sh[r];
         }
-    uint8_t* slot = lds + kRows * kPitch + wave * kTileBytes;
-    v4i acc[3][MT];
+    uint8_t* slot = lds + kRows * kPitch + wave * BW * kTileBytes;
+    v4i acc[3][BW][MT];
 #pragma unroll
     for (int k = 0; k < 3; ++k)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[k][mt] = v4i{0, 0, 0, 0};
+        for (int b = 0; b < BW; ++b)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[k][b][mt] = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int u = 0; u < P; ++u) {
-        *reinterpret_cast<v4u*>(slot + 64 * (lane & 15) + 16 * (lane >> 4)) = wt[u];
-        wave_lds_fence();
-        uint32_t bw[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) bw[w] = *reinterpret_cast<const uint32_t*>(slot + 256 * w + 4 * lane);
+        for (int b = 0; b < BW; ++b)
+            *reinterpret_cast<v4u*>(slot + b * kTileBytes + 64 * (lane & 15) + 16 * (lane >> 4)) =
+                wt[b][u];
+        wave_lds_fence();
+        uint32_t bw[BW][4];
+#pragma unroll
+        for (int b = 0; b < BW; ++b)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                bw[b][w] = *reinterpret_cast<const uint32_t*>(slot + b * kTileBytes + 256 * w + 4 * lane);
         wave_lds_fence();
         const uint8_t* arow_u = lds + j * kPitch + u * kTileK + 16 * g;
 #define BAND_STEP(F, ACC)                                                                         \
         {                                                                                         \
-            const v4i b = v4i{field<F>(bw[0]), field<F>(bw[1]), field<F>(bw[2]), field<F>(bw[3])}; \
+            v4i bop[BW];                                                                          \
+            _Pragma("unroll") for (int b = 0; b < BW; ++b)                                        \
+                bop[b] = v4i{field<F>(bw[b][0]), field<F>(bw[b][1]), field<F>(bw[b][2]),          \
+                             field<F>(bw[b][3])};                                                 \
             _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                                   \
                 const v4i av = *reinterpret_cast<const v4i*>(arow_u + 16 * mt * kPitch +          \
                                                              64 * ((F) ^ (u & 3)));               \
-                acc[ACC][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, b, acc[ACC][mt], 0, 0, 0); \
+                _Pragma("unroll") for (int b = 0; b < BW; ++b)                                    \
+                    acc[ACC][b][mt] =                                                             \
+                        __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bop[b], acc[ACC][b][mt], 0, 0, 0); \
             }                                                                                     \
         }
         BAND_STEP(0, 0)
@@ -284,70 +359,107 @@ __global__ __launch_bounds__(kThreads) void gemm_band_kernel(
 #undef BAND_STEP
     }
 
-    // 4. Epilogue: lane (j, g), register v of m tile mt -> row m = 16 mt + 4 g + v, column n;
-    //    acc = a1 + a4 / 4 + a16 / 16 - 2 sum(x) (exact), then bf16(acc * ws / s)
-    //    by epilogue_bf16_scaled's argument, for all the lane's outputs at
-    //    once: one ballot for the midpoints, then the stores.
-    int total[MT][4];
-    float fv[MT][4];
+    // 4. Epilogue: lane (j, g), register v of m tile mt of band b -> row
+    //    m = m0 + 16 mt + 4 g + v, column n[b]; acc = a1 + a4 / 4 + a16 / 16
+    //    - 2 sum(x) (exact), then bf16(acc * ws / s) by epilogue_bf16_scaled's
+    //    argument, for all the lane's outputs at once: one ballot for the
+    //    midpoints, then the stores.
+    int total[BW][MT][4];
+    float fv[BW][MT][4];
+    bool mid[BW][MT][4];
     bool redo = false;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int t[4] = {acc[0][mt].x + (acc[1][mt].x >> 2) + (acc[2][mt].x >> 4),
-                          acc[0][mt].y + (acc[1][mt].y >> 2) + (acc[2][mt].y >> 4),
-                          acc[0][mt].z + (acc[1][mt].z >> 2) + (acc[2][mt].z >> 4),
-                          acc[0][mt].w + (acc[1][mt].w >> 2) + (acc[2][mt].w >> 4)};
+    for (int b = 0; b < BW; ++b)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            total[mt][v] = t[v] + offset[mt][v];
-            fv[mt][v] = static_cast<float>(static_cast<double>(total[mt][v]) * cs[mt][v]);
-            redo |= ((__float_as_uint(fv[mt][v]) & 0xFFFFu) == 0x8000u) || __builtin_isnan(fv[mt][v]);
+        for (int mt = 0; mt < MT; ++mt) {
+            const v4i* c = acc[0][b] + mt;
+            const v4i* c4 = acc[1][b] + mt;
+            const v4i* c16 = acc[2][b] + mt;
+            const int t[4] = {c->x + (c4->x >> 2) + (c16->x >> 4), c->y + (c4->y >> 2) + (c16->y >> 4),
+                              c->z + (c4->z >> 2) + (c16->z >> 4), c->w + (c4->w >> 2) + (c16->w >> 4)};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                total[b][mt][v] = t[v] + offset[mt][v];
+                fv[b][mt][v] = static_cast<float>(static_cast<double>(total[b][mt][v]) * cs[b][mt][v]);
+                mid[b][mt][v] = ((__float_as_uint(fv[b][mt][v]) & 0xFFFFu) == 0x8000u) ||
+                                __builtin_isnan(fv[b][mt][v]);
+                redo |= mid[b][mt][v];
+            }
         }
-    }
-    uint16_t out[MT][4];
+    uint16_t out[BW][MT][4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int b = 0; b < BW; ++b)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) out[mt][v] = static_cast<uint16_t>(cvt_pk_bf16(fv[mt][v], 0.0f));
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                out[b][mt][v] = static_cast<uint16_t>(cvt_pk_bf16(fv[b][mt][v], 0.0f));
+    // Only the outputs that a lane needs are redone, each under its own
+    // ballot: a wavefront that meets a midpoint (about one in 64 at 16
+    // outputs a lane) runs one exact division, not one per output.  Redoing
+    // all 16 took 5.2 us against 1.3 us for the epilogue (M = 64, 13824 x
+    // 2560), and those wavefronts ended the launch.
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(redo) != 0, 0)) {
         asm volatile("");   // kept a branch: if-converted it would cost every output its division
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int b = 0; b < BW; ++b)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) out[mt][v] = epilogue_bf16(total[mt][v], wsf, sm[mt][v]);
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (__builtin_amdgcn_ballot_w64(mid[b][mt][v]) != 0) {
+                        asm volatile("");
+                        out[b][mt][v] = epilogue_bf16(total[b][mt][v], wsf[b], sm[mt][v]);
+                    }
     }
-    if (n < N) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+    for (int b = 0; b < BW; ++b) {
+        if (n[b] < N) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = 16 * mt + 4 * g + v;
-                if (m < M) {
-                    const size_t o = static_cast<size_t>(m) * N + n;
-                    y[o] = out[mt][v];
-                    if (acc_out) acc_out[o] = total[mt][v];
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = m0 + 16 * mt + 4 * g + v;
+                    if (m < M) {
+                        const size_t o = static_cast<size_t>(m) * N + n[b];
+                        y[o] = out[b][mt][v];
+                        if (acc_out) acc_out[o] = total[b][mt][v];
+                    }
                 }
-            }
+        }
     }
 }
 
 using BandFn = void (*)(const int8_t*, const v4u*, const float*, const uint16_t*, uint32_t, int,
                         uint16_t*, int32_t*, int, int, int);
 
-template <int MT, int... Ps>
+template <int MT, int BW, int... Ps>
 constexpr std::array<BandFn, sizeof...(Ps)> band_table(std::integer_sequence<int, Ps...>) {
-    return {{&gemm_band_kernel<MT, Ps + 1>...}};
+    return {{&gemm_band_kernel<MT, Ps + 1, BW>...}};
 }
 
 constexpr int kBandMaxSteps = kBandMaxK / kTileK;
-// [MT - 1][P - 1]
-const std::array<std::array<BandFn, kBandMaxSteps>, 2> kBandKernels = {{
-    band_table<1>(std::make_integer_sequence<int, kBandMaxSteps>{}),
-    band_table<2>(std::make_integer_sequence<int, kBandMaxSteps>{}),
+
+// The instances: m tiles per row group and bands per wavefront.
+struct BandShape {
+    int mt, bw;
+};
+constexpr std::array<BandShape, 3> kBandShapes = {{{1, 1}, {2, 1}, {2, 2}}};
+
+// [shape][P - 1]
+const std::array<std::array<BandFn, kBandMaxSteps>, 3> kBandKernels = {{
+    band_table<1, 1>(std::make_integer_sequence<int, kBandMaxSteps>{}),
+    band_table<2, 1>(std::make_integer_sequence<int, kBandMaxSteps>{}),
+    band_table<2, 2>(std::make_integer_sequence<int, kBandMaxSteps>{}),
 }};
 
-size_t band_lds_bytes(int mt, int P) {
-    return static_cast<size_t>(16 * mt) * (P * kTileK + kRowPad) + kBands * kTileBytes;
+// M <= 16: one m tile; M <= 32: two; M = 33 .. 64: row groups of 32 rows with
+// two bands per wavefront (all 64 rows of K = 2560 would need 165 KB of LDS).
+int band_shape_of(int M) { return M <= 16 ? 0 : M <= 32 ? 1 : 2; }
+
+size_t band_lds_bytes(const BandShape& sh, int P) {
+    return static_cast<size_t>(16 * sh.mt) * (P * kTileK + kRowPad) +
+           static_cast<size_t>(kWaves * sh.bw) * kTileBytes;
 }
 
 }  // namespace
@@ -356,27 +468,30 @@ hipError_t launch_gemm_band(const int8_t* xq, const uint8_t* packed, const float
                             const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int M,
                             int N, int K, hipStream_t stream) {
     if (M < 2 || M > kBandMaxM || K > kBandMaxK) return hipErrorInvalidValue;
-    const int mt = (M + 15) / 16;
+    const int shape = band_shape_of(M);
+    const BandShape& sh = kBandShapes[shape];
     const int P = (K + kTileK - 1) / kTileK;
-    const BandFn fn = kBandKernels[mt - 1][P - 1];
-    const size_t lds = band_lds_bytes(mt, P);
-    // Staged rows beyond 64 KiB of LDS (M > 16 at K = 2560) need the
-    // kernel's dynamic-LDS limit raised, once per kernel.
-    static std::array<std::array<std::once_flag, kBandMaxSteps>, 2> raised;
-    static std::array<std::array<hipError_t, kBandMaxSteps>, 2> raised_status;
-    std::call_once(raised[mt - 1][P - 1], [&] {
-        raised_status[mt - 1][P - 1] = hipFuncSetAttribute(
+    const BandFn fn = kBandKernels[shape][P - 1];
+    const size_t lds = band_lds_bytes(sh, P);
+    // Staged rows beyond 64 KiB of LDS (more than 16 rows at K = 2560) need
+    // the kernel's dynamic-LDS limit raised, once per kernel.
+    static std::array<std::array<std::once_flag, kBandMaxSteps>, 3> raised;
+    static std::array<std::array<hipError_t, kBandMaxSteps>, 3> raised_status;
+    std::call_once(raised[shape][P - 1], [&] {
+        raised_status[shape][P - 1] = hipFuncSetAttribute(
             reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
             static_cast<int>(lds));
     });
-    if (raised_status[mt - 1][P - 1] != hipSuccess) return raised_status[mt - 1][P - 1];
+    if (raised_status[shape][P - 1] != hipSuccess) return raised_status[shape][P - 1];
     uint32_t seg_mul;
     int seg_shift;
     seg_divisor(N / ws_num, seg_mul, seg_shift);
     const int nbands = (N + kTileRows - 1) / kTileRows;
-    const unsigned groups = static_cast<unsigned>((nbands + kBands - 1) / kBands);
-    fn<<<groups, kThreads, lds, stream>>>(xq, reinterpret_cast<const v4u*>(packed), s, ws, seg_mul,
-                                          seg_shift, y, acc, M, N, K);
+    const int groups = (nbands + kWaves * sh.bw - 1) / (kWaves * sh.bw);
+    const int H = sh.bw;                                  // row groups, as the kernel takes them
+    if (M > 16 * sh.mt * H) return hipErrorInvalidValue;
+    fn<<<static_cast<unsigned>(groups * H), kThreads, lds, stream>>>(
+        xq, reinterpret_cast<const v4u*>(packed), s, ws, seg_mul, seg_shift, y, acc, M, N, K);
     return hipGetLastError();
 }
 

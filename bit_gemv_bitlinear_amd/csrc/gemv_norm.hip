@@ -71,28 +71,6 @@ __device__ __forceinline__ double bf16_f64(uint32_t b) {
     return static_cast<double>(__uint_as_float(b << 16));
 }
 
-// bf16 rounding (nearest, ties to even) of an fp64 value in two hardware
-// steps: to fp32 rounded to odd, then fp32 to bf16 with ties to even.  An
-// intermediate format with at least two more significant bits than the
-// target makes that pair equal to one direct rounding (Boldo and Melquiond,
-// "Emulation of FMA and correctly rounded sums: proved algorithms using
-// rounding to odd", IEEE Trans. Computers 57(4), 2008); fp32 carries 24 bits
-// against bf16's 8, also among the subnormals (quantum 2^-149 against
-// 2^-133), and shares bf16's exponent range, so a value beyond it lands on
-// fp32's largest finite value, which rounds on to infinity as it should.
-// Rounding to odd: the nearest fp32 (the conversion's own rounding, ties to
-// even, with fp32 subnormals kept), and when that is inexact and even, its
-// neighbour on the other side of the value, which is odd.  NaN gives the
-// quiet NaN 0x7FC0.
-__device__ __forceinline__ uint32_t bf16_rne_f64(double d) {
-    const float f = static_cast<float>(d);
-    uint32_t u = __float_as_uint(f);
-    const double back = static_cast<double>(f);
-    if (back != d && !(u & 1u)) u += fabs(back) > fabs(d) ? 0xFFFFFFFFu : 1u;
-    u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    return d != d ? 0x7FC0u : u;
-}
-
 // Eight fp64 values to bf16 (nearest, ties to even) by way of fp32: one
 // conversion to fp32, one to bf16.  Every bf16 midpoint is an fp32 number,
 // so the first rounding can land on one but never step across one: the two

@@ -166,8 +166,9 @@ hipError_t launch_gemm_prefill(const int8_t* xq, const uint8_t* packed, const fl
                                int N, int K, hipStream_t stream);
 
 // 2 <= M <= kBandMaxM and K <= kBandMaxK: int8 MFMA with one wavefront per
-// 16-row band over all of K and the activation rows staged in LDS.
-constexpr int kBandMaxM = 32;
+// one or two 16-row bands over all of K and the activation rows (or a group
+// of 32 of them) staged in LDS.
+constexpr int kBandMaxM = 64;
 constexpr int kBandMaxK = 2560;
 hipError_t launch_gemm_band(const int8_t* xq, const uint8_t* packed, const float* s,
                             const uint16_t* ws, int ws_num, uint16_t* y, int32_t* acc, int M,

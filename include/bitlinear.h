@@ -192,9 +192,10 @@ int quantize_act_absmax_i8(const void* x, int x_dtype, int8_t* q, float* s, int 
  * y approximates x . w^T * ws.
  * M == 1 with K <= 61440 runs the GEMV kernel (workgroups of 1, 2 or 4
  * 16-row bands, v_dot8 on masked codes and nibble-split activations).
- * 2 <= M <= 32 with K <= 2560 (a few sequences decoded together) runs the
+ * 2 <= M <= 64 with K <= 2560 (a few sequences decoded together) runs the
  * band kernel: int8 MFMA
- * (v_mfma_i32_16x16x64_i8), one wavefront per 16 weight rows over all of K,
+ * (v_mfma_i32_16x16x64_i8), one wavefront per 16 weight rows over all of K
+ * (two per wavefront, with the rows in two workgroups of 32, for M > 32),
  * the activation rows staged once per workgroup in LDS.  M >= 65 with
  * N >= 8192 (prompt processing on wide layers, the prompt lengths of
  * [W2A8] §7.2) runs the LDS-tiled int8 MFMA kernel (workgroup tiles of up

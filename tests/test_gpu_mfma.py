@@ -60,35 +60,45 @@ def test_shapes(bl, M, N, K):
 
 @pytest.mark.parametrize("M,N,K,ws_num", [(3, 16, 16, 1), (2, 1, 2560, 1), (31, 1000, 2304, 4),
                                           (32, 13824, 2560, 2), (20, 100, 2560, 4), (9, 4096, 256, 8),
-                                          (24, 48, 1040, 3)])
+                                          (24, 48, 1040, 3),
+                                          (33, 13824, 2560, 2), (47, 1030, 2304, 2), (64, 2432, 272, 1),
+                                          (40, 24, 1040, 3), (64, 2048, 2560, 4), (50, 128, 16, 1)])
 def test_band_kernel_shapes(bl, M, N, K, ws_num):
-    # 2 <= M <= 32 with K <= 2560 runs one wavefront per 16-row band: one
-    # 256-K tile or ten, a single output row, rows not filling the last
-    # workgroup, weight-scale segments that split bands, K not a multiple of 256
+    # 2 <= M <= 64 with K <= 2560 runs the band kernel: one 256-K tile or ten,
+    # a single output row, rows not filling the last workgroup, weight-scale
+    # segments that split bands, K not a multiple of 256.  M = 33 .. 64 takes
+    # two bands per wavefront and two groups of 32 rows, whose workgroup ids
+    # are 8 apart within runs of 8 band groups: whole runs (2048 rows), runs
+    # and a tail of 1 .. 7 groups (1030: 9 groups; 2432: 19), only a tail (24,
+    # 128 rows), and a second group of 1 .. 31 rows (33, 47, 50)
     c = synth.make_int8_gemv(f"band_m{M}", M, N, K, ws_num, synth.seed_for(8, 1, M + N % 97))
     check(bl, c.name, c.w, c.xq, c.s, c.ws, c.ws_num)
 
 
-def test_extremes_and_segments(bl):
+@pytest.mark.parametrize("M", [32, 64])
+def test_extremes_and_segments(bl, M):
+    # the largest sums of either sign in both row groups (M = 64: rows 32 .. 34)
     g = synth.rng(515)
-    M, N, K = 32, 64 * 4, 2560
+    N, K = 64 * 4, 2560
     w = synth.ternary_uniform(g, N, K)
     w[:64] = 1
     w[64:128] = -1
     xq = synth.int8_uniform(g, M, K, -128, 127)
-    xq[0] = -128
-    xq[1] = 127
-    xq[2] = 0
+    for r0 in range(0, M, 32):
+        xq[r0] = -128
+        xq[r0 + 1] = 127
+        xq[r0 + 2] = 0
     s = synth.act_scale(g, M)
-    check(bl, "extremes_ws4", w, xq, s, synth.ws_bits(g, 4), 4)
+    check(bl, f"extremes_ws4_m{M}", w, xq, s, synth.ws_bits(g, 4), 4)
 
 
-@pytest.mark.parametrize("M,N", [(48, 640), (16, 1000), (32, 13824)])
-def test_bf16_entry_with_staging(bl, M, N):
+@pytest.mark.parametrize("M,N,K", [(48, 640, 2560), (16, 1000, 2560), (32, 13824, 2560),
+                                   (40, 640, 4096)])
+def test_bf16_entry_with_staging(bl, M, N, K):
     # the bf16 entry quantises into q_out / s_out, then runs the layer kernel
-    # for M >= 2: the band kernel for M = 16, 32, the streaming kernel for 48
+    # for M >= 2: the band kernel for K <= 2560 (M = 48: two row groups), the
+    # streaming kernel for K = 4096
     import torch
-    K = 2560
     c = synth.make_float_gemv(f"bf16_m{M}", M, N, K, 2, 2718 + M, bf16=True)
     print(f"mfma bf16 entry M={M}", flush=True)
     packed = bl.pack_ternary_weights(dev(c.w))

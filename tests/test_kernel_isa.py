@@ -233,18 +233,18 @@ def band_asm(tmp_path_factory):
 
 
 def test_band_kernels_issue_rows_then_weights(band_asm):
-    # gemm_band_kernel<MT, P>: every activation load (buffer loads: P chunks
-    # per thread for one m tile, 4 ceil(P / 2) for two), then all P weight
-    # tiles (non-temporal 16-byte loads), before the first wait on vector
-    # memory -- the rows first, since a wait for them counts every load
-    # issued before them; no scratch, and the static LDS is the rows' scales
-    # and sums (fp64 + fp32 + int32 per row)
-    kernels = list(re.finditer(r"^(_ZN\S*gemm_band_kernelILi(\d)ELi(\d+)E\S*):", band_asm, re.M))
-    assert sorted((int(m.group(2)), int(m.group(3))) for m in kernels) == \
-        [(mt, p) for mt in (1, 2) for p in range(1, 11)]
+    # gemm_band_kernel<MT, P, BW>: every activation load (buffer loads: P
+    # chunks per thread for one m tile, 4 ceil(P / 2) for two), then all BW P
+    # weight tiles (non-temporal 16-byte loads), before the first wait on
+    # vector memory -- the rows first, since a wait for them counts every
+    # load issued before them; no scratch, and the static LDS is the rows'
+    # scales and sums (fp64 + fp32 + int32 per row)
+    kernels = list(re.finditer(r"^(_ZN\S*gemm_band_kernelILi(\d)ELi(\d+)ELi(\d)E\S*):", band_asm, re.M))
+    assert sorted((int(m.group(2)), int(m.group(4)), int(m.group(3))) for m in kernels) == \
+        [(mt, bw, p) for mt, bw in ((1, 1), (2, 1), (2, 2)) for p in range(1, 11)]
     late = []
     for m in kernels:
-        name, MT, P = m.group(1), int(m.group(2)), int(m.group(3))
+        name, MT, P, BW = m.group(1), int(m.group(2)), int(m.group(3)), int(m.group(4))
         body = band_asm[m.end():band_asm.index("s_endpgm", m.end())]
         first_wait = body.index("s_waitcnt vmcnt")
         head = body[:first_wait]
@@ -252,8 +252,8 @@ def test_band_kernels_issue_rows_then_weights(band_asm):
         weights = [w.start() for w in re.finditer(r"global_load_dwordx4 [^\n]* nt\b", head)]
         last_row = max(r.start() for r in re.finditer(r"buffer_load_dwordx4 ", head))
         want_rows = P if MT == 1 else 4 * ((P + 1) // 2)
-        if rows != want_rows or len(weights) != P or min(weights) < last_row:
-            late.append((MT, P, rows, len(weights)))
+        if rows != want_rows or len(weights) != BW * P or min(weights) < last_row:
+            late.append((MT, P, BW, rows, len(weights)))
         assert _meta(band_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
         assert _meta(band_asm, name, "amdhsa_group_segment_fixed_size") == 16 * MT * (8 + 4 + 4), name
-    assert not late, f"(MT, P, row loads, weight loads before the first wait, rows first): {late}"
+    assert not late, f"(MT, P, BW, row loads, weight loads before the first wait, rows first): {late}"
