@@ -12,11 +12,32 @@
 #include <algorithm>
 #include <iterator>
 #include <map>
+#include <mutex>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "bitlinear.h"
 #include "kernels.hpp"
+
+namespace bl {
+
+hipError_t raise_lds_limit(const void* fn, int bytes) {
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, hipError_t> raised;   // (kernel, device) -> status
+    const std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(fn, dev);
+    auto it = raised.find(key);
+    if (it == raised.end())
+        it = raised.emplace(key, hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     bytes)).first;
+    return it->second;
+}
+
+}  // namespace bl
 
 namespace {
 

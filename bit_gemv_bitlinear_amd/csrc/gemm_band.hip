@@ -48,7 +48,6 @@
 //     bf16 midpoint.
 #include <algorithm>
 #include <array>
-#include <mutex>
 #include <utility>
 
 #include "gemv_core.hpp"
@@ -474,15 +473,11 @@ hipError_t launch_gemm_band(const int8_t* xq, const uint8_t* packed, const float
     const BandFn fn = kBandKernels[shape][P - 1];
     const size_t lds = band_lds_bytes(sh, P);
     // Staged rows beyond 64 KiB of LDS (more than 16 rows at K = 2560) need
-    // the kernel's dynamic-LDS limit raised, once per kernel.
-    static std::array<std::array<std::once_flag, kBandMaxSteps>, 3> raised;
-    static std::array<std::array<hipError_t, kBandMaxSteps>, 3> raised_status;
-    std::call_once(raised[shape][P - 1], [&] {
-        raised_status[shape][P - 1] = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-            static_cast<int>(lds));
-    });
-    if (raised_status[shape][P - 1] != hipSuccess) return raised_status[shape][P - 1];
+    // the kernel's dynamic-LDS limit raised, once per kernel and device.
+    if (lds > 65536) {
+        const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(fn), static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
     uint32_t seg_mul;
     int seg_shift;
     seg_divisor(N / ws_num, seg_mul, seg_shift);

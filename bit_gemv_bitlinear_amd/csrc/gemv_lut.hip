@@ -36,7 +36,6 @@
 // Bound: LDS lookups and VALU (8 lookups per packed word against 4 dot4 in
 // the dot-product kernel); the weights stream from HBM as there.
 #include <array>
-#include <mutex>
 #include <utility>
 
 #include "gemv_core.hpp"
@@ -249,15 +248,13 @@ hipError_t launch_gemv_lut(const int8_t* xq, const uint8_t* packed, const float*
     const unsigned groups = static_cast<unsigned>((nbands + B - 1) / B);
     const size_t lds = static_cast<size_t>(S) * 16 * kLutChunkStride;
     // Tables beyond 64 KiB (K > 3840) need the kernel's dynamic-LDS limit
-    // raised, once per kernel.
-    static std::array<std::once_flag, kLutMaxSteps> raised;
-    hipError_t attr = hipSuccess;
-    std::call_once(raised[P - 1], [&] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kLutKernels[P - 1]),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   static_cast<int>(kLutMaxK / kTileK * 16 * kLutChunkStride));
-    });
-    if (attr != hipSuccess) return attr;
+    // raised (to the largest table), once per kernel and device.
+    if (lds > 65536) {
+        const hipError_t attr =
+            raise_lds_limit(reinterpret_cast<const void*>(kLutKernels[P - 1]),
+                            static_cast<int>(kLutMaxK / kTileK * 16 * kLutChunkStride));
+        if (attr != hipSuccess) return attr;
+    }
     uint32_t seg_mul;
     int seg_shift;
     seg_divisor(N / ws_num, seg_mul, seg_shift);

@@ -24,6 +24,11 @@ hipError_t launch_quant(const void* x, int x_is_bf16, int8_t* q, float* s, int M
 // exact for every 0 <= n < 2^24.
 void seg_divisor(int d, uint32_t& mul, int& shift);
 
+// Raise kernel fn's dynamic-LDS limit to `bytes` on the current device, once
+// per kernel and device (kernels whose LDS exceeds the default 64 KiB); the
+// status of that one call, every time.
+hipError_t raise_lds_limit(const void* fn, int bytes);
+
 // M == 1 GEMV geometry: `waves` wavefronts per workgroup covering `bands`
 // 16-row bands, `steps` K steps (256 K each) per wavefront; waves == 0 when
 // K is beyond the GEMV kernels (K > kGemvMaxK), which then leave M == 1 to

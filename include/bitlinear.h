@@ -30,8 +30,10 @@
  *   - No call allocates or frees device memory except bl_graph_create /
  *     bl_graph_destroy (graph objects and their work tables), so calls on
  *     different streams may run concurrently when their outputs do not
- *     overlap.  The only state the library keeps is the table-lookup GEMV's
- *     once-per-device raise of its kernels' LDS limit.
+ *     overlap.  The only state the library keeps: which kernels have had
+ *     their dynamic-LDS limit raised on which device (those staging more
+ *     than 64 KiB: the batched kernel above 16 rows, the table-lookup GEMV
+ *     above K = 3840), and the allocation-free ternariser's histogram.
  *   - Alignment: xq, x, packed and q_out 16 bytes; s, s_out, acc 4 bytes;
  *     ws, y 2 bytes.  Otherwise BL_ERR_ALIGN.
  *   - Shapes: 1 <= M <= 1048576, N >= 1, K >= 16 with K % 16 == 0,

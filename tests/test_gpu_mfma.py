@@ -75,6 +75,21 @@ def test_band_kernel_shapes(bl, M, N, K, ws_num):
     check(bl, c.name, c.w, c.xq, c.s, c.ws, c.ws_num)
 
 
+@pytest.mark.parametrize("M,N", [(64, 13824), (33, 1030), (20, 13824)])
+def test_band_kernel_without_acc(bl, M, N):
+    # y alone (no int32 output), as the bench and most callers run it; the
+    # rows of both row groups and a ragged last band
+    import torch
+    K = 2560
+    c = synth.make_int8_gemv(f"band_y_m{M}", M, N, K, 2, synth.seed_for(8, 2, M + N % 89))
+    print(f"mfma band y only M={M} N={N}", flush=True)
+    packed = bl.pack_ternary_weights(dev(c.w))
+    y = bl.bitlinear_i8xi2(dev(c.xq), packed, dev(c.s), bf16_dev(c.ws), N, 2)
+    torch.cuda.synchronize()
+    _, y_o = oracle.bitlinear_i8(c.xq, c.w, c.s, c.ws, 2)
+    assert assert_bf16_close(host_bits(y), y_o, max_ulp=1) == 0
+
+
 @pytest.mark.parametrize("M", [32, 64])
 def test_extremes_and_segments(bl, M):
     # the largest sums of either sign in both row groups (M = 64: rows 32 .. 34)
