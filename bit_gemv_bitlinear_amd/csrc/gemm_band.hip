@@ -31,12 +31,13 @@
 //     registers (measured: M = 16 staging 640 ns vs 755 ns as quads; M = 32
 //     1090 ns as quads vs 1490 ns as chunks);
 //   * a tile reaches the MFMA B layout through a wavefront-private 1 KiB LDS
-//     slot: lane l (rows 4 (l / 16) .. +3 of K chunk l % 16) stores its 16
-//     bytes at 64 (l % 16) + 16 (l / 16), so that lane (j, g) finds the word
-//     of row j, K chunk 4v + g at 256 v + 64 g + 4 j -- 64 consecutive dwords
-//     per read, free of bank conflicts (two slots used in turn, so that the
-//     next tile's round trip overlaps this tile's MFMAs, measured slower: the
-//     loop runs at the pace the weights arrive);
+//     slot per band: lane l (rows 4 (l / 16) .. +3 of K chunk l % 16) stores
+//     its 16 bytes at 64 (l % 16) + 16 (l / 16), so that lane (j, g) finds
+//     the word of row j, K chunk 4v + g at 256 v + 64 g + 4 j -- 64
+//     consecutive dwords per read, free of bank conflicts (two slots used in
+//     turn, so that the next tile's round trip overlaps this tile's MFMAs,
+//     measured slower at M = 16 / 32, where the loop runs at the pace the
+//     weights arrive, and no faster at M = 64);
 //   * the codes stay unsigned (c = w + 2) and each 2-bit field is masked in
 //     place: MFMA f takes field f of the lane's four words (chunks g, g + 4,
 //     g + 8, g + 12), so all of its bytes carry the factor 4^f (field 3 is
@@ -44,8 +45,8 @@
 //     the activations are staged so that the matching operand of lane (i, g)
 //     is 16 contiguous bytes, and the +2 offset goes with the rows' sums;
 //   * epilogue per output: y = bf16(acc * ws[n] / s[m]) through the fp64
-//     product and fp32 (as epilogue_bf16_scaled), exact division only at a
-//     bf16 midpoint.
+//     product and fp32 (as epilogue_bf16_scaled), the exact division only for
+//     an output whose fp32 value is a bf16 midpoint.
 #include <algorithm>
 #include <array>
 #include <utility>
@@ -106,13 +107,15 @@ __device__ __forceinline__ void split_group_id(int id, int groups, int& bg, int&
 
 // MT = m tiles of 16 rows per row group; P = 256-K tiles per band (= ceil(K / 256));
 // BW = bands per wavefront.  BW = 1: one row group (M <= 16 MT); BW = 2: two
-// row groups of 16 MT rows (M = 33 .. 64 with MT = 2).  (Two per band, each dotting half the tiles and
-// handing its sums to the other through LDS, measured slower at 13824 x 2560:
-// M = 16 4.76 -> 5.07 us, M = 32 5.91 -> 6.46 us, with an earlier decode.
-// Four more wavefronts that only stage the activations, so that the bands'
-// weight loads go out at once, measured slower still -- M = 16 4.44 -> 5.37
-// us: a CU returns its loads in the order they were issued, so the rows
-// then arrive behind the weights.)
+// row groups of 16 MT rows (M = 33 .. 64 with MT = 2).
+// (Two wavefronts per band, each dotting half the tiles and handing its sums
+// to the other through LDS, measured slower at 13824 x 2560: M = 16 4.76 ->
+// 5.07 us, M = 32 5.91 -> 6.46 us with an earlier decode, and M = 32 / 64
+// 5.81 / 8.98 -> 6.75 / 9.08 us with this one.  Four more wavefronts that
+// only stage the activations, so that the bands' weight loads go out at
+// once, measured slower still -- M = 16 4.44 -> 5.37 us: a CU returns its
+// loads in the order they were issued, so the rows then arrive behind the
+// weights.)
 template <int MT, int P, int BW>
 __global__ __launch_bounds__(kThreads) void gemm_band_kernel(
     const int8_t* __restrict__ xq, const v4u* __restrict__ packed, const float* __restrict__ s,
