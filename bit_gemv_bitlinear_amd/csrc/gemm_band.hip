@@ -212,7 +212,12 @@ __global__ __launch_bounds__(kThreads) void gemm_band_kernel(
         }
     }
     // The activation loads go out first, so that a wait for them leaves the
-    // weight loads in flight.
+    // weight loads in flight, and those of every wavefront before any
+    // wavefront's weights (a barrier without a wait: the loads are issued,
+    // not complete), so that no row queues behind another wavefront's
+    // weights.  Same box: M = 16 / 64 4.28 / 8.97 -> 4.23 / 8.94 us.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // Tile u of every band goes out before tile u + 1 of any, in the order
     // the loop below waits for them.
