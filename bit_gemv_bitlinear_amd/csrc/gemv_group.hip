@@ -82,6 +82,13 @@ __device__ __forceinline__ void group_body(const GroupWork& g, int4* __restrict_
             xv[2 * c + 1] = as_uint4(x16[2 * q + 1]);
         }
     }
+    // Every wavefront's row loads go out before any wavefront's weight loads
+    // (a barrier without a wait: the loads are issued, not complete), so
+    // that no row queues behind another wavefront's weights.  The decode
+    // step, six pairs of runs on one box: 85.2 -> 82.7 us on average.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     const global_ptr<const v4u> tiles =
         global(reinterpret_cast<const v4u*>(g.packed)) + static_cast<size_t>(band) * S * 64 + lane;
     v4u w[2][P];
