@@ -368,11 +368,11 @@ def chained_step(bl):
         nbytes += 2 * c["K"] + (2 * c["N"] if c.get("residual") is not None else 0)
     g = bl.ChainedDecodeGraph(calls)
     ms = time_replays(g.launch, 10)
-    kernels = g.kernels
+    kernels, linked = g.kernels, g.linked
     g.close()
     return {"us_per_step": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "bytes_per_step": nbytes, "projections_per_step": len(calls),
-            "kernels_per_step": kernels}
+            "kernels_per_step": kernels, "hand_offs_per_step": linked}
 
 
 def dispatch_probe(bl, n=400, sleep_cycles=400_000_000):

@@ -48,6 +48,7 @@ SIGNATURES = {
     "bl_graph_launch": (_I, [_P, _P]),
     "bl_graph_size": (_I, [_P]),
     "bl_graph_kernels": (_I, [_P]),
+    "bl_graph_linked": (_I, [_P]),
     "bl_graph_destroy": (_I, [_P]),
 }
 
@@ -406,3 +407,8 @@ class ChainedDecodeGraph(DecodeGraph):
         h = ctypes.c_void_p()
         _check(lib().bl_graph_create_norm(arr, len(calls), ctypes.byref(h)), "bl_graph_create_norm")
         self._h = h
+
+    @property
+    def linked(self):
+        """Calls that take the activation and its norm statistics from the call before them."""
+        return lib().bl_graph_linked(self._h)

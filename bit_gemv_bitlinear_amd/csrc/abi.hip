@@ -151,7 +151,8 @@ struct bl_graph {
     hipGraphExec_t exec;
     int n;                          // calls the graph holds
     int kernels;                    // kernel launches per replay
-    std::vector<void*> tables;      // device work tables of its grouped launches
+    std::vector<void*> tables;      // device memory it owns: work tables, hand-off buffers
+    int linked = 0;                 // calls that take a hand-off from the call before
 };
 
 namespace {
@@ -191,7 +192,7 @@ int capture_graph(int n_calls, int n_launch, std::vector<void*>& tables, bl_grap
         free_tables(tables);
         return rc;
     }
-    bl_graph* g = new (std::nothrow) bl_graph{exec, n_calls, n_launch, {}};
+    bl_graph* g = new (std::nothrow) bl_graph{exec, n_calls, n_launch, {}, 0};
     if (!g) {
         (void)hipGraphExecDestroy(exec);
         free_tables(tables);
@@ -549,6 +550,43 @@ int bl_graph_create_norm(const bl_norm_desc* descs, int n, bl_graph** out) {
         }
     }
     std::vector<void*> tables;
+    auto device_alloc = [&](size_t bytes) -> void* {
+        void* p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
+        tables.push_back(p);
+        return p;
+    };
+    // Hand-offs: a GLU call whose x and x_up are the two halves of the y of
+    // the call just before it, both launched on their own, takes its row m
+    // and its statistics from that call's epilogue (buffers the graph owns).
+    std::vector<bl::NormLink> links(launches.size(), bl::NormLink{});
+    int linked = 0;
+    for (size_t li = 1; li < launches.size(); ++li) {
+        const NormLaunch& L = launches[li];
+        const NormLaunch& Lp = launches[li - 1];
+        if (L.calls.size() != 1 || Lp.calls.size() != 1) continue;
+        const int c = L.calls[0], pc = Lp.calls[0];
+        const bl_norm_desc& d = descs[c];
+        const bl_norm_desc& dp = descs[pc];
+        if (!d.x_up || d.x != dp.y || d.x_up != dp.y + d.K) continue;
+        if (!bl::norm_link_supported(plans[pc], d.K)) continue;
+        uint16_t* m = static_cast<uint16_t*>(device_alloc(2u * static_cast<size_t>(d.K)));
+        bl::NormPart* parts = static_cast<bl::NormPart*>(
+            m ? device_alloc(sizeof(bl::NormPart) * plans[pc].groups) : nullptr);
+        if (!parts) {
+            free_tables(tables);
+            return BL_ERR_HIP;
+        }
+        links[li - 1].m_out = m;
+        links[li - 1].gamma_next = d.gamma;
+        links[li - 1].part_out = parts;
+        links[li - 1].half = d.K;
+        links[li].n_part = plans[pc].groups;
+        links[li].part_in = parts;
+        plans[c] = bl::norm_plan(m, nullptr, d.gamma, d.eps, d.packed, d.ws, d.ws_num, d.residual,
+                                 d.y, nullptr, nullptr, nullptr, nullptr, d.N, d.K);
+        ++linked;
+    }
     for (NormLaunch& L : launches) {
         if (L.calls.size() < 2) continue;
         std::vector<bl::NormWork> work;
@@ -575,16 +613,15 @@ int bl_graph_create_norm(const bl_norm_desc* descs, int n, bl_graph** out) {
         L.table = static_cast<const bl::NormWork*>(p);
         L.n_work = static_cast<int>(work.size());
     }
-    return capture_graph(n, static_cast<int>(launches.size()), tables, out,
-                         [&](int li, hipStream_t cs) {
+    const int rc = capture_graph(n, static_cast<int>(launches.size()), tables, out,
+                                 [&](int li, hipStream_t cs) {
         const NormLaunch& L = launches[li];
         if (L.table)
             return status_of(bl::launch_gemv_norm_group(L.key, L.table, L.n_work, L.lds, cs));
-        const bl_norm_desc& d = descs[L.calls[0]];
-        return status_of(bl::launch_gemv_norm(d.x, d.x_up, d.gamma, d.eps, d.packed, d.ws,
-                                              d.ws_num, d.residual, d.y, nullptr, nullptr,
-                                              nullptr, nullptr, d.N, d.K, cs));
+        return status_of(bl::launch_gemv_norm_plan(plans[L.calls[0]], links[li], cs));
     });
+    if (rc == BL_OK) (*out)->linked = linked;
+    return rc;
 }
 
 int bl_graph_launch(bl_graph* graph, hipStream_t stream) {
@@ -595,6 +632,8 @@ int bl_graph_launch(bl_graph* graph, hipStream_t stream) {
 int bl_graph_size(const bl_graph* graph) { return graph ? graph->n : BL_ERR_NULL; }
 
 int bl_graph_kernels(const bl_graph* graph) { return graph ? graph->kernels : BL_ERR_NULL; }
+
+int bl_graph_linked(const bl_graph* graph) { return graph ? graph->linked : BL_ERR_NULL; }
 
 int bl_graph_destroy(bl_graph* graph) {
     if (!graph) return BL_OK;

@@ -163,12 +163,19 @@ __device__ __forceinline__ uint4 row_load(RowBuf r, int chunk) {
 // budget.
 constexpr int kNormMaxWaves = 8;
 
+// What the prologue starts from: the row x itself, the relu2-GLU of x and
+// x_up, or a row m handed off by the previous projection with its
+// statistics (NormLink).
+enum : int { kNormPlain = 0, kNormGlu = 1, kNormLinked = 2 };
+
 // One workgroup's bands of one projection: the body of the single-call kernel
 // (group = its block index) and of the grouped kernel (group = the index in
 // its work record).  The pointers are cast to the global address space: the
 // grouped kernel reads them from memory, not from its kernel arguments.
-template <int P, int C, bool GLU>
-__device__ __forceinline__ void norm_body(const NormArgs& a, int group) {
+template <int P, int C, int MODE>
+__device__ __forceinline__ void norm_body(const NormArgs& a, const NormLink& l, int group) {
+    constexpr bool GLU = MODE == kNormGlu;
+    constexpr bool LINKED = MODE == kNormLinked;
     extern __shared__ int4 act[];   // Wb*P*16 16-byte chunks: the int8 row, zero-padded
     __shared__ int part_sh[kNormMaxWaves][64];
     __shared__ int xsum_sh[kNormMaxWaves];
@@ -185,7 +192,15 @@ __device__ __forceinline__ void norm_body(const NormArgs& a, int group) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nbands = (N + kTileRows - 1) / kTileRows;
-    const int band = min(group * B + (wave >> lw), nbands - 1);
+    // The workgroup's j-th band: the next B bands, or, for a projection that
+    // hands the GLU off, B / 2 gate bands and the up bands of the same rows.
+    const int hb = l.half / kTileRows;   // the first up band (0: no hand-off)
+    const int hB = B >> 1;
+    auto band_at = [&](int j) {
+        if (hb == 0) return group * B + j;
+        return j < hB ? group * hB + j : hb + group * hB + (j - hB);
+    };
+    const int band = min(band_at(wave >> lw), nbands - 1);
     const int S = (K + kTileK - 1) / kTileK;
     const int s0 = (wave & (Wb - 1)) * P;
     const int n16 = K >> 4;
@@ -194,12 +209,25 @@ __device__ __forceinline__ void norm_body(const NormArgs& a, int group) {
 
     // 1. The inputs of this thread's output row (weight scale, residual),
     //    the cached chunks of the row (x, x_up, gamma), then every weight load.
-    const int n_out = group * B * kTileRows + tid;   // tid < 16*B writes
+    const int n_out = band_at(min(tid >> 4, B - 1)) * kTileRows + (tid & 15);   // tid < 16*B writes
     const uint32_t n_c = static_cast<uint32_t>(min(n_out, N - 1));
     const uint16_t wsb = global(a.ws)[(static_cast<uint64_t>(n_c) * a.seg_mul) >> a.seg_shift];
     // unconditional (a branch would end in a wait for this load); the weight
-    // scales stand in as a source when there is no residual
+    // scales stand in as a source when there is no residual, and when there
+    // is no hand-off for the next projection's gamma at this lane's gate row
     const uint16_t resb = global(a.residual ? a.residual : a.ws)[a.residual ? n_c : 0u];
+    const uint16_t gnb = global(l.m_out ? l.gamma_next : a.ws)[
+        l.m_out ? static_cast<uint32_t>(min(n_out, l.half - 1)) : 0u];
+    // The hand-off's partials (a consumer): four 16-byte loads per lane, the
+    // ones past n_part reading as zeros (the buffer's range check).
+    v4u part[LINKED ? kNormMaxParts / 64 : 1];
+    if constexpr (LINKED) {
+        const RowBuf rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<NormPart*>(l.part_in), 0,
+                                                            16 * l.n_part, kRawBufferFlags);
+#pragma unroll
+        for (int k = 0; k < kNormMaxParts / 64; ++k)
+            part[k] = __builtin_amdgcn_raw_buffer_load_b128(rp, (lane + 64 * k) * 16, 0, 0);
+    }
     const global_ptr<const v4u> x16 = global(reinterpret_cast<const v4u*>(a.x));
     const global_ptr<const v4u> u16 = global(reinterpret_cast<const v4u*>(a.x_up));
     const global_ptr<const v4u> g16 = global(reinterpret_cast<const v4u*>(a.gamma));
@@ -250,30 +278,46 @@ __device__ __forceinline__ void norm_body(const NormArgs& a, int group) {
     double pv[C][8];
 #pragma unroll
     for (int c = 0; c < C; ++c) products8(m_chunk(c, tid + c * nthreads), gv[c], pv[c], ssq, pm);
-    for (int idx = tid + C * nthreads; idx < n_in; idx += nthreads) {
-        double pt[8];
-        products8(m_chunk(C, idx), to_uint4(g16[idx]), pt, ssq, pm);
-    }
-    ssq = wave_sum_f64(ssq);
-    pm = wave_max_u32(pm);
-    if (lane == 0) {
-        ssq_sh[wave] = ssq;
-        pm_sh[wave] = pm;
-    }
-    __syncthreads();
 
     // 3. The inverse RMS and the activation scale.  Rounding is monotone and
     //    inv > 0, so the largest |xn| is the bf16 rounding of pmax * inv: the
-    //    absmax needs no pass over xn.  The partial sums are added in wave
-    //    order; all eight slots are read at once and the unused ones dropped.
+    //    absmax needs no pass over xn.
     double total_sq = 0.0;
-    pm = 0;
+    if constexpr (LINKED) {
+        // From the producer's partials, added in the same order by every
+        // wavefront (each lane's four in turn, then across the lanes): no
+        // barrier and no pass over the row.
+        double sp = 0.0;
+        uint32_t up = 0;
 #pragma unroll
-    for (int i = 0; i < kNormMaxWaves; ++i) {
-        const double v = ssq_sh[i];
-        const uint32_t u = pm_sh[i];
-        total_sq += i < W ? v : 0.0;
-        pm = max(pm, i < W ? u : 0u);
+        for (int k = 0; k < kNormMaxParts / 64; ++k) {
+            sp += __hiloint2double(static_cast<int>(part[k].y), static_cast<int>(part[k].x));
+            up = max(up, part[k].z);
+        }
+        total_sq = wave_sum_f64(sp);
+        pm = wave_max_u32(up);
+    } else {
+        for (int idx = tid + C * nthreads; idx < n_in; idx += nthreads) {
+            double pt[8];
+            products8(m_chunk(C, idx), to_uint4(g16[idx]), pt, ssq, pm);
+        }
+        ssq = wave_sum_f64(ssq);
+        pm = wave_max_u32(pm);
+        if (lane == 0) {
+            ssq_sh[wave] = ssq;
+            pm_sh[wave] = pm;
+        }
+        __syncthreads();
+        // The wavefronts' partial sums are added in wave order; all eight
+        // slots are read at once and the unused ones dropped.
+        pm = 0;
+#pragma unroll
+        for (int i = 0; i < kNormMaxWaves; ++i) {
+            const double v = ssq_sh[i];
+            const uint32_t u = pm_sh[i];
+            total_sq += i < W ? v : 0.0;
+            pm = max(pm, i < W ? u : 0u);
+        }
     }
     const double inv = 1.0 / sqrt(total_sq / static_cast<double>(K) + a.eps);
     const double pmax = __hiloint2double(static_cast<int>(pm), 0);
@@ -333,41 +377,69 @@ __device__ __forceinline__ void norm_body(const NormArgs& a, int group) {
         const int firstw = min(bw, B - 1) << lw;
         int total = offset;
         for (int j = 0; j < Wb; ++j) total += part_sh[firstw + j][slot];
+        uint32_t o = 0;
         if (bw < B && n_out < N) {
-            uint16_t o = epilogue_bf16_scaled(total, cs, bf16_to_float(wsb), sm);
+            o = epilogue_bf16_scaled(total, cs, bf16_to_float(wsb), sm);
             if (a.residual)   // the fp64 sum of two bf16 values rounds to bf16 as the exact sum does
-                o = static_cast<uint16_t>(bf16_rne_f64(static_cast<double>(bf16_to_float(resb)) +
-                                                       static_cast<double>(bf16_to_float(o))));
-            global(a.y)[n_out] = o;
+                o = bf16_rne_f64(static_cast<double>(bf16_to_float(static_cast<uint16_t>(resb))) +
+                                 static_cast<double>(bf16_to_float(static_cast<uint16_t>(o))));
+            global(a.y)[n_out] = static_cast<uint16_t>(o);
             if (a.acc) global(a.acc)[n_out] = total;
+        }
+        if (l.m_out != nullptr) {
+            // The hand-off: lanes 0 .. 8B-1 hold gate rows, lanes 8B .. 16B-1
+            // the up rows of the same index.  m = bf16(max(gate, 0)^2 * up),
+            // exact in fp64 before the rounding; then the workgroup's sum of
+            // m^2 and largest |m * gamma_next| (both exact per value in fp64),
+            // as the consumer's prologue would have computed them.
+            const int hl = 8 * B;
+            const uint32_t ub = static_cast<uint32_t>(__shfl(static_cast<int>(o), lane + hl));
+            double sq = 0.0;
+            uint32_t pmv = 0;
+            if (lane < hl) {
+                const double g = bf16_f64(o);
+                const double gr = g > 0.0 ? g : 0.0;
+                const uint32_t mb = bf16_rne_f64(gr * gr * bf16_f64(ub));
+                global(l.m_out)[n_out] = static_cast<uint16_t>(mb);
+                const double m = bf16_f64(mb);
+                sq = m * m;
+                pmv = static_cast<uint32_t>(__double2hiint(m * bf16_f64(gnb))) & 0x7FFFFFFFu;
+            }
+            sq = wave_sum_f64(sq);
+            pmv = wave_max_u32(pmv);
+            if (lane == 0)
+                global(reinterpret_cast<v4u*>(l.part_out))[group] =
+                    v4u{static_cast<uint32_t>(__double2loint(sq)),
+                        static_cast<uint32_t>(__double2hiint(sq)), pmv, 0u};
         }
     }
 }
 
-template <int P, int C, bool GLU>
-__global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(NormArgs a) {
-    norm_body<P, C, GLU>(a, static_cast<int>(blockIdx.x));
+template <int P, int C, int MODE>
+__global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_kernel(NormArgs a, NormLink l) {
+    norm_body<P, C, MODE>(a, l, static_cast<int>(blockIdx.x));
 }
 
 // Several projections of one kernel instance in one launch: workgroup i runs
 // the bands of work record i (its projection's arguments and its group).
-template <int P, int C, bool GLU>
+// No hand-off here.
+template <int P, int C, int MODE>
 __global__ __launch_bounds__(kNormMaxWaves * 64) void gemv_norm_group_kernel(
     const NormWork* __restrict__ work) {
     const NormWork& w = work[blockIdx.x];
-    norm_body<P, C, GLU>(w.a, w.group);
+    norm_body<P, C, MODE>(w.a, NormLink{}, w.group);
 }
 
-using GemvNormFn = void (*)(NormArgs);
+using GemvNormFn = void (*)(NormArgs, NormLink);
 using GemvNormGroupFn = void (*)(const NormWork*);
-template <int C, bool GLU, int... Ps>
+template <int C, int MODE, int... Ps>
 constexpr std::array<GemvNormFn, sizeof...(Ps)> norm_table(std::integer_sequence<int, Ps...>) {
-    return {{&gemv_norm_kernel<Ps + 1, C, GLU>...}};
+    return {{&gemv_norm_kernel<Ps + 1, C, MODE>...}};
 }
-template <int C, bool GLU, int... Ps>
+template <int C, int MODE, int... Ps>
 constexpr std::array<GemvNormGroupFn, sizeof...(Ps)> norm_group_table(
     std::integer_sequence<int, Ps...>) {
-    return {{&gemv_norm_group_kernel<Ps + 1, C, GLU>...}};
+    return {{&gemv_norm_group_kernel<Ps + 1, C, MODE>...}};
 }
 // P = 1 .. kNormMaxSteps (rows up to kNormMaxK over at most kNormMaxWaves
 // wavefronts per band) and C = 1 or 2 cached chunks per thread; the loop over
@@ -375,19 +447,21 @@ constexpr std::array<GemvNormGroupFn, sizeof...(Ps)> norm_group_table(
 constexpr int kNormMaxSteps = 16;
 using NormRow = std::array<GemvNormFn, kNormMaxSteps>;
 using NormGroupRow = std::array<GemvNormGroupFn, kNormMaxSteps>;
-// [glu][C - 1][P - 1]
-const std::array<std::array<NormRow, 2>, 2> kNormKernels = {{
-    {{norm_table<1, false>(std::make_integer_sequence<int, kNormMaxSteps>{}),
-      norm_table<2, false>(std::make_integer_sequence<int, kNormMaxSteps>{})}},
-    {{norm_table<1, true>(std::make_integer_sequence<int, kNormMaxSteps>{}),
-      norm_table<2, true>(std::make_integer_sequence<int, kNormMaxSteps>{})}},
-}};
-const std::array<std::array<NormGroupRow, 2>, 2> kNormGroupKernels = {{
-    {{norm_group_table<1, false>(std::make_integer_sequence<int, kNormMaxSteps>{}),
-      norm_group_table<2, false>(std::make_integer_sequence<int, kNormMaxSteps>{})}},
-    {{norm_group_table<1, true>(std::make_integer_sequence<int, kNormMaxSteps>{}),
-      norm_group_table<2, true>(std::make_integer_sequence<int, kNormMaxSteps>{})}},
-}};
+template <int MODE>
+constexpr std::array<NormRow, 2> norm_rows() {
+    return {{norm_table<1, MODE>(std::make_integer_sequence<int, kNormMaxSteps>{}),
+             norm_table<2, MODE>(std::make_integer_sequence<int, kNormMaxSteps>{})}};
+}
+template <int MODE>
+constexpr std::array<NormGroupRow, 2> norm_group_rows() {
+    return {{norm_group_table<1, MODE>(std::make_integer_sequence<int, kNormMaxSteps>{}),
+             norm_group_table<2, MODE>(std::make_integer_sequence<int, kNormMaxSteps>{})}};
+}
+// [mode][C - 1][P - 1]
+const std::array<std::array<NormRow, 2>, 3> kNormKernels = {
+    {norm_rows<kNormPlain>(), norm_rows<kNormGlu>(), norm_rows<kNormLinked>()}};
+const std::array<std::array<NormGroupRow, 2>, 2> kNormGroupKernels = {
+    {norm_group_rows<kNormPlain>(), norm_group_rows<kNormGlu>()}};
 
 // The geometry of gemv_shape with at most kNormMaxWaves wavefronts per
 // workgroup: fewer wavefronts per band (longer runs) or fewer bands.
@@ -433,6 +507,25 @@ NormPlan norm_plan(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamm
     return p;
 }
 
+bool norm_link_supported(const NormPlan& p, int half) {
+    // whole bands in each half, the same number of gate bands per workgroup
+    // in both, and at most kNormMaxParts workgroups
+    const int B = p.args.B;
+    return p.groups > 0 && p.groups <= kNormMaxParts && half > 0 && p.args.N == 2 * half &&
+           half % kTileRows == 0 && B % 2 == 0 && (half / kTileRows) % (B / 2) == 0;
+}
+
+hipError_t launch_gemv_norm_plan(const NormPlan& p, const NormLink& link, hipStream_t stream) {
+    if (p.groups == 0) return hipErrorInvalidValue;
+    if (link.m_out && !norm_link_supported(p, link.half)) return hipErrorInvalidValue;
+    if (link.part_in && (p.glu || link.n_part < 1 || link.n_part > kNormMaxParts))
+        return hipErrorInvalidValue;
+    const int mode = link.part_in ? kNormLinked : p.glu ? kNormGlu : kNormPlain;
+    const GemvNormFn fn = kNormKernels[mode][p.cached - 1][p.steps - 1];
+    fn<<<static_cast<unsigned>(p.groups), p.threads, p.lds, stream>>>(p.args, link);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamma,
                             float eps, const uint8_t* packed, const uint16_t* ws, int ws_num,
                             const uint16_t* residual, uint16_t* y, uint16_t* xn_out,
@@ -440,15 +533,13 @@ hipError_t launch_gemv_norm(const uint16_t* x, const uint16_t* x_up, const uint1
                             hipStream_t stream) {
     const NormPlan p = norm_plan(x, x_up, gamma, eps, packed, ws, ws_num, residual, y, xn_out,
                                  q_out, s_out, acc, N, K);
-    if (p.groups == 0) return hipErrorInvalidValue;
-    const GemvNormFn fn = kNormKernels[p.glu ? 1 : 0][p.cached - 1][p.steps - 1];
-    fn<<<static_cast<unsigned>(p.groups), p.threads, p.lds, stream>>>(p.args);
-    return hipGetLastError();
+    return launch_gemv_norm_plan(p, NormLink{}, stream);
 }
 
 hipError_t launch_gemv_norm_group(const NormPlan& key, const NormWork* work, int n_work,
                                   size_t lds, hipStream_t stream) {
-    const GemvNormGroupFn fn = kNormGroupKernels[key.glu ? 1 : 0][key.cached - 1][key.steps - 1];
+    const GemvNormGroupFn fn =
+        kNormGroupKernels[key.glu ? kNormGlu : kNormPlain][key.cached - 1][key.steps - 1];
     fn<<<static_cast<unsigned>(n_work), key.threads, lds, stream>>>(work);
     return hipGetLastError();
 }

@@ -155,6 +155,36 @@ NormPlan norm_plan(const uint16_t* x, const uint16_t* x_up, const uint16_t* gamm
 hipError_t launch_gemv_norm_group(const NormPlan& key, const NormWork* work, int n_work,
                                   size_t lds, hipStream_t stream);
 
+// A hand-off between two projections of a chain: the one whose output holds
+// the gate half [0, half) and the up half [half, 2 half) of the MLP computes,
+// in its epilogue, the activation m of the next projection and, per
+// workgroup, the two statistics the next projection's RMSNorm needs (the sum
+// of m^2 and the largest |m * gamma| as the high word of its fp64 encoding).
+// The next projection then reads m as its row and the partials instead of
+// recomputing them in every workgroup.
+struct alignas(16) NormPart {
+    double ssq;
+    uint32_t pm;
+    uint32_t pad;
+};
+constexpr int kNormMaxParts = 256;   // partials one consumer reads (4 per lane)
+struct NormLink {
+    // producer (m_out null: none); its workgroups each take half / 16 / (B / 2)
+    // gate bands and the up bands of the same rows
+    uint16_t* m_out;
+    const uint16_t* gamma_next;
+    NormPart* part_out;
+    int half;
+    // consumer (part_in null: none): the row is m, its statistics the
+    // producer's n_part partials
+    int n_part;
+    const NormPart* part_in;
+};
+// Whether a projection of plan p can produce the GLU hand-off for rows of
+// `half` values (its output is the two halves).
+bool norm_link_supported(const NormPlan& p, int half);
+hipError_t launch_gemv_norm_plan(const NormPlan& p, const NormLink& link, hipStream_t stream);
+
 // Ternarise a bf16 N x K matrix by its mean |w| and pack it; scales[0..2] =
 // ws, s, mean (bf16); workspace: 256 uint64 (the exponent histogram).
 hipError_t launch_ternarize(const uint16_t* w, uint8_t* packed, uint16_t* scales,

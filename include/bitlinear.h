@@ -338,6 +338,20 @@ int bl_graph_create(const bl_gemv_desc* descs, int n, bl_graph** out);
  * may overlap none of its other inputs (BL_ERR_ARG).  Same rules and errors
  * as bl_graph_create otherwise, with bitlinear_rmsnorm_i8xi2's checks per
  * descriptor.
+ * Hand-off ([W2A8] §4.1: w13 feeds the activation before ffn_sub_norm and
+ * w2): when a call with x_up reads as x and x_up the two halves of the y of
+ * the call just before it (that call's N = 2K, each half whole 16-row
+ * bands, the two calls launched on their own, the earlier in at most 256
+ * workgroups), the earlier call's kernel also computes, in its epilogue,
+ * m = bf16(max(gate, 0)^2 * up) and, per workgroup, the sum of m^2 and the
+ * largest |m * gamma| of the later call; the later call reads m and those
+ * partials instead of redoing the activation and the reductions in each of
+ * its workgroups.  The results are the same bits (the sum of squares is
+ * added in another order, as the kernel's own order already differs from
+ * left to right).  The graph allocates 2K bytes and 16 bytes per producing
+ * workgroup of device memory for each hand-off here and frees them in
+ * bl_graph_destroy; replays of one graph must not overlap (they share these
+ * buffers, as they share the calls' outputs).
  */
 typedef struct bl_norm_desc {
     const uint16_t* x;        /* device, bf16, K */
@@ -363,6 +377,10 @@ int bl_graph_size(const bl_graph* graph);
 
 /* Number of kernel launches one replay of the graph makes, or BL_ERR_NULL. */
 int bl_graph_kernels(const bl_graph* graph);
+
+/* Number of calls of a bl_graph_create_norm graph that take the hand-off from
+ * the call before them (0 for bl_graph_create graphs), or BL_ERR_NULL. */
+int bl_graph_linked(const bl_graph* graph);
 
 /* Destroy the graph (NULL is allowed).  The caller ensures no replay is in flight. */
 int bl_graph_destroy(bl_graph* graph);

@@ -171,8 +171,10 @@ def test_chained_two_layers_as_graph(bl):
     graph = bl.ChainedDecodeGraph(calls)
     assert len(graph) == 4 * n_layers
     # per layer: qkv and o (independent, one kernel instance) share a launch,
-    # then gate+up, then down
+    # then gate+up, then down, which takes the activation and its statistics
+    # from gate+up's epilogue
     assert graph.kernels == 3 * n_layers
+    assert graph.linked == n_layers
     # oracle chain
     want, hb = [], h0
     for L in layers:
@@ -235,6 +237,95 @@ def test_independent_projections_share_a_launch(bl):
     for (name, *_), c, wv in zip(specs, calls, want):
         np.testing.assert_array_equal(host_bits(c["y"]), wv, err_msg=name)
     graph.close()
+
+
+def _chain_case(bl, g, specs, ws0=None, x0=None):
+    # specs: (N, K, ws_num, src, residual) per call; src "ext" reads a fresh row,
+    # "halves" the two halves of the previous call's y as (x, x_up), "swapped"
+    # them the other way round.  ws0 / x0 replace the first call's weight
+    # scales / row.
+    import torch
+    calls, want, prev = [], [], None
+    for i, (N, K, wn, src, res) in enumerate(specs):
+        w = synth.ternary_uniform(g, N, K)
+        ws = synth.ws_bits(g, wn) if i or ws0 is None else ws0
+        gam = oracle.bf16_rne(1.0 + 0.1 * g.normal(size=K))
+        r = synth.normal_bf16_bits(g, 1, N).reshape(-1) if res else None
+        c = dict(gamma=bf16_dev(gam), packed=bl.pack_ternary_weights(dev(w)), ws=bf16_dev(ws),
+                 ws_num=wn, y=torch.full((N,), float("nan"), dtype=torch.bfloat16, device="cuda"),
+                 N=N, K=K)
+        if src == "ext":
+            x, up = synth.normal_bf16_bits(g, 1, K).reshape(-1), None
+            if i == 0 and x0 is not None:
+                x = x0
+            c["x"] = bf16_dev(x)
+        else:
+            (pc, pw) = prev
+            lo, hi = (slice(0, K), slice(K, 2 * K)) if src == "halves" else (slice(K, 2 * K), slice(0, K))
+            c["x"], c["x_up"] = pc["y"][lo], pc["y"][hi]
+            x, up = pw[lo], pw[hi]
+        if res:
+            c["residual"] = bf16_dev(r)
+        yw = oracle.norm_bitlinear(x, gam, w, ws, wn, up_bits=up, residual_bits=r)[4]
+        calls.append(c)
+        want.append(yw)
+        prev = (c, yw)
+    return calls, want
+
+
+def _replay_and_check(bl, label, calls, want, linked, reps=2):
+    import torch
+    print(f"chained graph: hand-off {label}", flush=True)
+    graph = bl.ChainedDecodeGraph(calls)
+    assert graph.kernels == len(calls)
+    assert graph.linked == linked
+    for rep in range(reps):
+        for c in calls:
+            c["y"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.launch()
+        torch.cuda.synchronize()
+        for i, (c, wv) in enumerate(zip(calls, want)):
+            np.testing.assert_array_equal(host_bits(c["y"]), wv, err_msg=f"{label} call {i} rep {rep}")
+    graph.close()
+
+
+@pytest.mark.parametrize("case", ["b2_256_parts", "producer_and_consumer", "swapped", "b1_small",
+                                  "model_shape_ws2"])
+def test_glu_hand_off(bl, case):
+    # The GLU projection takes m and its statistics from the call before it
+    # when it reads that call's y as (gate, up): a producer of two bands per
+    # workgroup (8192 rows: 256 workgroups, the most partials a consumer
+    # reads) with residuals on both sides; a call that takes one hand-off and
+    # gives the next (producer of two bands, consumer rows of 6912 and 4096);
+    # halves swapped, and a producer of one band per workgroup, which do not
+    # link; the model's gate+up and down with split weight scales.
+    g = synth.rng(synth.seed_for(6, 60, len(case)))
+    specs, linked = {
+        "b2_256_parts": ([(8192, 512, 1, "ext", True), (100, 4096, 1, "halves", True)], 1),
+        "producer_and_consumer": ([(13824, 2560, 2, "ext", False), (8192, 6912, 1, "halves", False),
+                                   (300, 4096, 3, "halves", True)], 2),
+        "swapped": ([(13824, 2560, 2, "ext", False), (2560, 6912, 1, "swapped", True)], 0),
+        "b1_small": ([(128, 256, 1, "ext", False), (48, 64, 1, "halves", False)], 0),
+        "model_shape_ws2": ([(13824, 2560, 2, "ext", False), (2560, 6912, 2, "halves", True)], 1),
+    }[case]
+    calls, want = _chain_case(bl, g, specs)
+    _replay_and_check(bl, case, calls, want, linked)
+
+
+@pytest.mark.parametrize("edge", ["zeros", "tiny", "huge"])
+def test_glu_hand_off_edge_rows(bl, edge):
+    # The hand-off over extreme activations, set through gate+up's input row
+    # and weight scale: a zero row (m = 0, the consumer's row all zeros), a
+    # weight scale of 2^-52 (m subnormal or zero), one of 2^30 (m up to about
+    # 1e34, squares far beyond fp32)
+    g = synth.rng(synth.seed_for(6, 61, len(edge)))
+    specs = [(13824, 2560, 1, "ext", False), (2560, 6912, 1, "halves", True)]
+    ws0 = {"zeros": None, "tiny": oracle.bf16_rne(np.array([2.0 ** -52])),
+           "huge": oracle.bf16_rne(np.array([2.0 ** 30]))}[edge]
+    x0 = np.zeros(2560, dtype=np.uint16) if edge == "zeros" else None
+    calls, want = _chain_case(bl, g, specs, ws0=ws0, x0=x0)
+    _replay_and_check(bl, f"edge rows {edge}", calls, want, 1, reps=1)
 
 
 def test_output_over_another_input_is_refused(bl):

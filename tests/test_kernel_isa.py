@@ -183,25 +183,29 @@ def test_prefill_no_scratch_and_declared_lds(prefill_asm):
         assert body.count("v_mfma_i32_16x16x64_i8") == 16 * MTW, name
 
 
-@pytest.mark.parametrize("kind", ["gemv_norm_kernel", "gemv_norm_group_kernel"])
-def test_norm_kernels_issue_all_loads_first(norm_asm, kind):
-    # gemv_norm_kernel<P, C, GLU> (one projection) and gemv_norm_group_kernel
-    # (several, one work record per workgroup): the row's C chunks of x,
-    # gamma (and x_up), buffer loads, and all P weight tiles are issued
-    # before the first wait, without scratch
-    kernels = list(re.finditer(r"^(_ZN\S*" + kind + r"ILi(\d+)ELi(\d)ELb([01])E\S*):", norm_asm, re.M))
-    assert len(kernels) == 64    # P = 1..16, C = 1, 2, with and without the GLU
+@pytest.mark.parametrize("kind,modes", [("gemv_norm_kernel", 3), ("gemv_norm_group_kernel", 2)])
+def test_norm_kernels_issue_all_loads_first(norm_asm, kind, modes):
+    # gemv_norm_kernel<P, C, MODE> (one projection; MODE 0 the row x, 1 its
+    # GLU with x_up, 2 a handed-off row with its partial statistics) and
+    # gemv_norm_group_kernel (several, one work record per workgroup; modes 0
+    # and 1): the row's C chunks of x, gamma (and x_up), the four 16-byte
+    # partial loads of mode 2, all buffer loads, and all P weight tiles are
+    # issued before the first wait, without scratch
+    kernels = list(re.finditer(r"^(_ZN\S*" + kind + r"ILi(\d+)ELi(\d)ELi([012])E\S*):", norm_asm, re.M))
+    assert len(kernels) == 32 * modes    # P = 1..16, C = 1, 2, each mode
+    assert {int(m.group(4)) for m in kernels} == set(range(modes))
     late = []
     for m in kernels:
-        name, P, C, glu = m.group(1), int(m.group(2)), int(m.group(3)), m.group(4) == "1"
+        name, P, C, mode = m.group(1), int(m.group(2)), int(m.group(3)), int(m.group(4))
         body = norm_asm[m.end():norm_asm.index("s_endpgm", m.end())]
         first_wait = body.index("s_waitcnt vmcnt")
         weights = len(re.findall(r"global_load_dwordx4 [^\n]* nt\b", body[:first_wait]))
-        rows = len(re.findall(r"buffer_load_dwordx4 ", body[:first_wait]))
-        if weights != P or rows != C * (3 if glu else 2):
-            late.append((P, C, glu, weights, rows))
+        # (the partials' unused fourth words make them dwordx3 loads)
+        rows = len(re.findall(r"buffer_load_dwordx[34] ", body[:first_wait]))
+        if weights != P or rows != C * (3 if mode == 1 else 2) + (4 if mode == 2 else 0):
+            late.append((P, C, mode, weights, rows))
         assert _meta(norm_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
-    assert not late, f"(P, C, glu, weight loads, row loads before the first wait): {late}"
+    assert not late, f"(P, C, mode, weight loads, row loads before the first wait): {late}"
 
 
 @pytest.fixture(scope="module")
