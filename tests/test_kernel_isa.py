@@ -190,7 +190,10 @@ def test_norm_kernels_issue_all_loads_first(norm_asm, kind, modes):
     # gemv_norm_group_kernel (several, one work record per workgroup; modes 0
     # and 1): the row's C chunks of x, gamma (and x_up), the four 16-byte
     # partial loads of mode 2, all buffer loads, and all P weight tiles are
-    # issued before the first wait, without scratch
+    # issued before the first wait, without scratch.  Before the first of
+    # those loads: no branch, and one round of argument reads (the work
+    # record's address, then the record, for the grouped kernel) -- a branch
+    # there had split the reads into rounds, each waiting for the last.
     kernels = list(re.finditer(r"^(_ZN\S*" + kind + r"ILi(\d+)ELi(\d)ELi([012])E\S*):", norm_asm, re.M))
     assert len(kernels) == 32 * modes    # P = 1..16, C = 1, 2, each mode
     assert {int(m.group(4)) for m in kernels} == set(range(modes))
@@ -204,6 +207,10 @@ def test_norm_kernels_issue_all_loads_first(norm_asm, kind, modes):
         rows = len(re.findall(r"buffer_load_dwordx[34] ", body[:first_wait]))
         if weights != P or rows != C * (3 if mode == 1 else 2) + (4 if mode == 2 else 0):
             late.append((P, C, mode, weights, rows))
+        pre = body[:min(body.index(k) for k in ("global_load", "buffer_load"))]
+        rounds = pre.count("s_waitcnt lgkmcnt")
+        if "s_cbranch" in pre or rounds != (2 if kind == "gemv_norm_group_kernel" else 1):
+            late.append((P, C, mode, "argument rounds", rounds, "branches", pre.count("s_cbranch")))
         assert _meta(norm_asm, name, "amdhsa_private_segment_fixed_size") == 0, name
     assert not late, f"(P, C, mode, weight loads, row loads before the first wait): {late}"
 
