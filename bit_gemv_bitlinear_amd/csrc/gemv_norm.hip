@@ -477,11 +477,17 @@ const std::array<std::array<NormGroupRow, 2>, 2> kNormGroupKernels = {
     {norm_group_rows<kNormPlain>(), norm_group_rows<kNormGlu>()}};
 
 // The geometry of gemv_shape with at most kNormMaxWaves wavefronts per
-// workgroup: fewer wavefronts per band (longer runs) or fewer bands.
+// workgroup: fewer wavefronts per band (longer runs) or fewer bands.  Wide
+// projections take half the GEMV's steps per wavefront: two wavefronts per
+// band share each workgroup's glue as well as the dot products (the chained
+// step's gate+up, 216 workgroups of 8 wavefronts: 457.2-457.9 -> 453.2-454.8
+// us; with 3 steps, 432 workgroups of 8, it is 538 us, and too many
+// workgroups for the hand-off to down).
+constexpr int kNormTargetSteps = 5;
 GemvShape norm_shape(int N, int K) {
     const int S = (K + kTileK - 1) / kTileK;
     const int nbands = (N + kTileRows - 1) / kTileRows;
-    const int target = nbands < kNarrowBands ? kTargetStepsNarrow : kTargetSteps;
+    const int target = nbands < kNarrowBands ? kTargetStepsNarrow : kNormTargetSteps;
     int Wb = 1;
     while (Wb < kNormMaxWaves && (S + Wb - 1) / Wb > target) Wb <<= 1;
     const int P = (S + Wb - 1) / Wb;

@@ -297,13 +297,13 @@ def test_glu_hand_off(bl, case):
     # when it reads that call's y as (gate, up): a producer of two bands per
     # workgroup (8192 rows: 256 workgroups, the most partials a consumer
     # reads) with residuals on both sides; a call that takes one hand-off and
-    # gives the next (producer of two bands, consumer rows of 6912 and 4096);
+    # gives the next (producers of two bands, consumer rows of 4096);
     # halves swapped, and a producer of one band per workgroup, which do not
     # link; the model's gate+up and down with split weight scales.
     g = synth.rng(synth.seed_for(6, 60, len(case)))
     specs, linked = {
         "b2_256_parts": ([(8192, 512, 1, "ext", True), (100, 4096, 1, "halves", True)], 1),
-        "producer_and_consumer": ([(13824, 2560, 2, "ext", False), (8192, 6912, 1, "halves", False),
+        "producer_and_consumer": ([(8192, 512, 2, "ext", False), (8192, 4096, 1, "halves", False),
                                    (300, 4096, 3, "halves", True)], 2),
         "swapped": ([(13824, 2560, 2, "ext", False), (2560, 6912, 1, "swapped", True)], 0),
         "b1_small": ([(128, 256, 1, "ext", False), (48, 64, 1, "halves", False)], 0),
