@@ -42,11 +42,16 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
     return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
                             __builtin_amdgcn_readlane(__double2loint(v), l));
 }
-__device__ __forceinline__ double wave_sum_f64(double v) {
+// The sum over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ double row_sum_f64(double v) {
     v += dpp_row_f64<kDppQuadXor1>(v);
     v += dpp_row_f64<kDppQuadXor2>(v);
     v += dpp_row_f64<kDppRowRor4>(v);
     v += dpp_row_f64<kDppRowRor8>(v);
+    return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v = row_sum_f64(v);
     return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
@@ -55,11 +60,15 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_row_u32(uint32_t v) {
     return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
     v = max(v, dpp_row_u32<kDppQuadXor1>(v));
     v = max(v, dpp_row_u32<kDppQuadXor2>(v));
     v = max(v, dpp_row_u32<kDppRowRor4>(v));
     v = max(v, dpp_row_u32<kDppRowRor8>(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = row_max_u32(v);
     const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
     const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
     return max(max(r0, r1), max(r2, r3));
@@ -393,9 +402,17 @@ __device__ __forceinline__ void norm_body(const NormArgs& a, const NormLink& l, 
             // the up rows of the same index.  m = bf16(max(gate, 0)^2 * up),
             // exact in fp64 before the rounding; then the workgroup's sum of
             // m^2 and largest |m * gamma_next| (both exact per value in fp64),
-            // as the consumer's prologue would have computed them.
+            // as the consumer's prologue would have computed them.  This is
+            // the end of the kernel's critical path, so it stays in vector
+            // registers: the up values come over by a lane swap (the upper
+            // half of the wavefront for B = 4, the odd rows for B = 2), and
+            // the totals by row reductions, row 0's added into row 1 for
+            // B = 4, stored by a lane that holds them.  Same box, the chained
+            // step: 454.0-454.6 -> 452.6-454.4 us.
             const int hl = 8 * B;
-            const uint32_t ub = static_cast<uint32_t>(__shfl(static_cast<int>(o), lane + hl));
+            const uint32_t ub =
+                hl == 32 ? __builtin_amdgcn_permlane32_swap(o, o, false, false)[1]
+                         : __builtin_amdgcn_permlane16_swap(o, o, false, false)[1];
             double sq = 0.0;
             uint32_t pmv = 0;
             if (lane < hl) {
@@ -407,9 +424,13 @@ __device__ __forceinline__ void norm_body(const NormArgs& a, const NormLink& l, 
                 sq = m * m;
                 pmv = static_cast<uint32_t>(__double2hiint(m * bf16_f64(gnb))) & 0x7FFFFFFFu;
             }
-            sq = wave_sum_f64(sq);
-            pmv = wave_max_u32(pmv);
-            if (lane == 0)
+            sq = row_sum_f64(sq);
+            pmv = row_max_u32(pmv);
+            if (hl == 32) {
+                sq += dpp_row_f64<kDppRowBcast15>(sq);
+                pmv = max(pmv, dpp_row_u32<kDppRowBcast15>(pmv));
+            }
+            if (lane == hl - 16)
                 global(reinterpret_cast<v4u*>(l.part_out))[group] =
                     v4u{static_cast<uint32_t>(__double2loint(sq)),
                         static_cast<uint32_t>(__double2hiint(sq)), pmv, 0u};
