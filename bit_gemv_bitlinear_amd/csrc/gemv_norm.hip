@@ -505,6 +505,13 @@ const std::array<std::array<NormGroupRow, 2>, 2> kNormGroupKernels = {
 // us; with 3 steps, 432 workgroups of 8, it is 538 us, and too many
 // workgroups for the hand-off to down).
 constexpr int kNormTargetSteps = 5;
+// Bands per workgroup are kept while at least this many workgroups remain
+// (the GEMV keeps 200): every workgroup redoes the glue over the whole row,
+// so fewer, wider workgroups share it.  qkv and o of the chained step take
+// two bands of four wavefronts per workgroup (120 + 80 workgroups, one
+// 16-byte chunk of the row per thread) instead of one (240 + 160, two
+// chunks for some threads): 452.1-453.8 -> 423.1-424.5 us per step, same box.
+constexpr int kNormMinGroups = 80;
 GemvShape norm_shape(int N, int K) {
     const int S = (K + kTileK - 1) / kTileK;
     const int nbands = (N + kTileRows - 1) / kTileRows;
@@ -514,7 +521,7 @@ GemvShape norm_shape(int N, int K) {
     const int P = (S + Wb - 1) / Wb;
     if (P > kNormMaxSteps) return GemvShape{0, 0, 0};
     int B = 4;
-    while (B > 1 && (nbands / B < kMinGroups || B * Wb > kNormMaxWaves)) B >>= 1;
+    while (B > 1 && (nbands / B < kNormMinGroups || B * Wb > kNormMaxWaves)) B >>= 1;
     return GemvShape{B * Wb, P, B};
 }
 

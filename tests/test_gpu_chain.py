@@ -206,7 +206,7 @@ def test_independent_projections_share_a_launch(bl):
     g = synth.rng(synth.seed_for(6, 50, 0))
     dim, ffn = synth.DIM, synth.FFN
     specs = [("qkv", 3840, dim, 1, False, None), ("o_inplace", dim, dim, 1, False, "inplace"),
-             ("o", dim, dim, 1, False, "separate"), ("ragged", 1000, dim, 4, False, None),
+             ("o", dim, dim, 1, False, "separate"), ("ragged", 2600, dim, 4, False, None),
              ("down", dim, ffn, 1, True, "separate")]
     calls, want = [], []
     for name, N, K, wn, glu, res in specs:
@@ -290,19 +290,20 @@ def _replay_and_check(bl, label, calls, want, linked, reps=2):
     graph.close()
 
 
-@pytest.mark.parametrize("case", ["b2_256_parts", "producer_and_consumer", "swapped", "b1_small",
+@pytest.mark.parametrize("case", ["b4_256_parts", "producer_and_consumer", "swapped", "b1_small",
                                   "model_shape_ws2"])
 def test_glu_hand_off(bl, case):
     # The GLU projection takes m and its statistics from the call before it
-    # when it reads that call's y as (gate, up): a producer of two bands per
-    # workgroup (8192 rows: 256 workgroups, the most partials a consumer
+    # when it reads that call's y as (gate, up): a producer of four bands per
+    # workgroup (16384 rows: 256 workgroups, the most partials a consumer
     # reads) with residuals on both sides; a call that takes one hand-off and
-    # gives the next (producers of two bands, consumer rows of 4096);
+    # gives the next (producers of four and of two bands per workgroup, the
+    # second in 256 workgroups; consumer rows of 4096);
     # halves swapped, and a producer of one band per workgroup, which do not
     # link; the model's gate+up and down with split weight scales.
     g = synth.rng(synth.seed_for(6, 60, len(case)))
     specs, linked = {
-        "b2_256_parts": ([(8192, 512, 1, "ext", True), (100, 4096, 1, "halves", True)], 1),
+        "b4_256_parts": ([(16384, 512, 1, "ext", True), (100, 8192, 1, "halves", True)], 1),
         "producer_and_consumer": ([(8192, 512, 2, "ext", False), (8192, 4096, 1, "halves", False),
                                    (300, 4096, 3, "halves", True)], 2),
         "swapped": ([(13824, 2560, 2, "ext", False), (2560, 6912, 1, "swapped", True)], 0),
