@@ -498,26 +498,27 @@ const std::array<std::array<NormGroupRow, 2>, 2> kNormGroupKernels = {
     {norm_group_rows<kNormPlain>(), norm_group_rows<kNormGlu>()}};
 
 // The geometry of gemv_shape with at most kNormMaxWaves wavefronts per
-// workgroup: fewer wavefronts per band (longer runs) or fewer bands.  Wide
-// projections take half the GEMV's steps per wavefront: two wavefronts per
-// band share each workgroup's glue as well as the dot products (the chained
-// step's gate+up, 216 workgroups of 8 wavefronts: 457.2-457.9 -> 453.2-454.8
-// us; with 3 steps, 432 workgroups of 8, it is 538 us, and too many
-// workgroups for the hand-off to down).
+// workgroup, and its own two constants, measured on the chained decode step.
+// Every workgroup redoes the glue over the whole row, so fewer, wider
+// workgroups share it:
+//  - runs of up to 5 steps per wavefront, whatever the width (the GEMV:
+//    10, or 4 below 400 bands).  gate+up takes two wavefronts per band
+//    (457.2-457.9 -> 453.2-454.8 us per step, same box; with 3 steps, 432
+//    workgroups: 538 us, and too many workgroups for the hand-off to down),
+//    qkv and o two per band instead of four (424.3-425.8 -> 420.6-421.4 us;
+//    down keeps eight: with four, two bands per workgroup, 447 us);
+//  - bands per workgroup kept down to 80 workgroups (the GEMV: 200).  qkv
+//    and o take two bands per workgroup, 120 + 80 workgroups instead of
+//    240 + 160 (452.1-453.8 -> 423.1-424.5 us; four bands, 60 + 40
+//    workgroups of eight wavefronts, 430 us).
 constexpr int kNormTargetSteps = 5;
-// Bands per workgroup are kept while at least this many workgroups remain
-// (the GEMV keeps 200): every workgroup redoes the glue over the whole row,
-// so fewer, wider workgroups share it.  qkv and o of the chained step take
-// two bands of four wavefronts per workgroup (120 + 80 workgroups, one
-// 16-byte chunk of the row per thread) instead of one (240 + 160, two
-// chunks for some threads): 452.1-453.8 -> 423.1-424.5 us per step, same box.
 constexpr int kNormMinGroups = 80;
+
 GemvShape norm_shape(int N, int K) {
     const int S = (K + kTileK - 1) / kTileK;
     const int nbands = (N + kTileRows - 1) / kTileRows;
-    const int target = nbands < kNarrowBands ? kTargetStepsNarrow : kNormTargetSteps;
     int Wb = 1;
-    while (Wb < kNormMaxWaves && (S + Wb - 1) / Wb > target) Wb <<= 1;
+    while (Wb < kNormMaxWaves && (S + Wb - 1) / Wb > kNormTargetSteps) Wb <<= 1;
     const int P = (S + Wb - 1) / Wb;
     if (P > kNormMaxSteps) return GemvShape{0, 0, 0};
     int B = 4;
