@@ -341,7 +341,10 @@ int bl_graph_create(const bl_gemv_desc* descs, int n, bl_graph** out);
  * Hand-off ([W2A8] §4.1: w13 feeds the activation before ffn_sub_norm and
  * w2): when a call with x_up reads as x and x_up the two halves of the y of
  * the call just before it (that call's N = 2K, each half whole 16-row
- * bands, the two calls launched on their own, the earlier in at most 256
+ * bands, the two calls launched on their own, and the earlier one's launch
+ * shape -- chosen from N and K alone -- an even number of bands per
+ * workgroup, at most 256 workgroups, and a whole number of workgroups in
+ * each half; the model's w13, 13824 x 2560, takes four bands in each of 216
  * workgroups), the earlier call's kernel also computes, in its epilogue,
  * m = bf16(max(gate, 0)^2 * up) and, per workgroup, the sum of m^2 and the
  * largest |m * gamma| of the later call; the later call reads m and those
