@@ -260,7 +260,11 @@ def _chain_case(bl, g, specs, ws0=None, x0=None):
                 x = x0
             c["x"] = bf16_dev(x)
         else:
-            (pc, pw) = prev
+            # "halves" / "swapped" of the previous call, or ("halves", i) of call i
+            if isinstance(src, tuple):
+                src, (pc, pw) = src[0], (calls[src[1]], want[src[1]])
+            else:
+                (pc, pw) = prev
             lo, hi = (slice(0, K), slice(K, 2 * K)) if src == "halves" else (slice(K, 2 * K), slice(0, K))
             c["x"], c["x_up"] = pc["y"][lo], pc["y"][hi]
             x, up = pw[lo], pw[hi]
@@ -273,11 +277,11 @@ def _chain_case(bl, g, specs, ws0=None, x0=None):
     return calls, want
 
 
-def _replay_and_check(bl, label, calls, want, linked, reps=2):
+def _replay_and_check(bl, label, calls, want, linked, reps=2, kernels=None):
     import torch
     print(f"chained graph: hand-off {label}", flush=True)
     graph = bl.ChainedDecodeGraph(calls)
-    assert graph.kernels == len(calls)
+    assert graph.kernels == (len(calls) if kernels is None else kernels)
     assert graph.linked == linked
     for rep in range(reps):
         for c in calls:
@@ -291,7 +295,7 @@ def _replay_and_check(bl, label, calls, want, linked, reps=2):
 
 
 @pytest.mark.parametrize("case", ["b4_256_parts", "producer_and_consumer", "swapped", "b1_small",
-                                  "model_shape_ws2"])
+                                  "model_shape_ws2", "grouped"])
 def test_glu_hand_off(bl, case):
     # The GLU projection takes m and its statistics from the call before it
     # when it reads that call's y as (gate, up): a producer of four bands per
@@ -300,7 +304,9 @@ def test_glu_hand_off(bl, case):
     # gives the next (producers of four and of two bands per workgroup, the
     # second in 256 workgroups; consumer rows of 4096);
     # halves swapped, and a producer of one band per workgroup, which do not
-    # link; the model's gate+up and down with split weight scales.
+    # link; the model's gate+up and down with split weight scales; and two
+    # producers sharing a grouped launch, each read by one of two consumers
+    # that share the next (no hand-off from or into a grouped launch).
     g = synth.rng(synth.seed_for(6, 60, len(case)))
     specs, linked = {
         "b4_256_parts": ([(16384, 512, 1, "ext", True), (100, 8192, 1, "halves", True)], 1),
@@ -309,9 +315,11 @@ def test_glu_hand_off(bl, case):
         "swapped": ([(13824, 2560, 2, "ext", False), (2560, 6912, 1, "swapped", True)], 0),
         "b1_small": ([(128, 256, 1, "ext", False), (48, 64, 1, "halves", False)], 0),
         "model_shape_ws2": ([(13824, 2560, 2, "ext", False), (2560, 6912, 2, "halves", True)], 1),
+        "grouped": ([(13824, 2560, 1, "ext", False), (13824, 2560, 2, "ext", False),
+                     (2560, 6912, 1, ("halves", 0), True), (2560, 6912, 1, ("halves", 1), False)], 0),
     }[case]
     calls, want = _chain_case(bl, g, specs)
-    _replay_and_check(bl, case, calls, want, linked)
+    _replay_and_check(bl, case, calls, want, linked, kernels=2 if case == "grouped" else None)
 
 
 @pytest.mark.parametrize("edge", ["zeros", "tiny", "huge"])
