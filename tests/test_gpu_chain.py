@@ -6,7 +6,8 @@ after attention_norm, o after attn_sub_norm plus the residual, gate+up after ffn
 down after relu(gate)^2 * up and ffn_sub_norm plus the residual -- compared output by
 output: the normalised row, its int8 quantisation and scale, the int32 accumulators and
 the bf16 result.  Then rows that are not multiples of the kernel's tiles, the smallest K,
-a zero row, a large-magnitude row, eps = 0, and a two-layer chain replayed as one graph.
+a zero row, a large-magnitude row, eps = 0, and chains of two layers and of the 30 the bench
+times replayed as one graph.
 The normalised row is defined in fp64; the kernel adds the squares in another order, which
 could in principle move a value by 1 ulp, but no input here does: every output is asserted
 exactly equal.
@@ -140,16 +141,24 @@ def test_bf16_midpoints(bl):
     check_proj(bl, "below midpoints", x, gamma, w, ws, 1, eps=np.float32(2.0 ** -28))
 
 
-def test_chained_two_layers_as_graph(bl):
+@pytest.mark.parametrize("n_layers", [2, synth.N_LAYERS])
+def test_chained_layers_as_graph(bl, n_layers):
+    # two layers, and the whole step the bench times (its layers, inputs and
+    # graph), every output of every layer checked on every replay
     import torch
-    n_layers = 2
-    layers = [synth.chained_layer(l) for l in range(n_layers)]
     h0 = synth.chained_h0()
-    print("chained graph: 2 layers x 4 projections", flush=True)
+    print(f"chained graph: {n_layers} layers x 4 projections", flush=True)
     dim, ffn = synth.DIM, synth.FFN
     h = [bf16_dev(h0)] + [torch.empty(dim, dtype=torch.bfloat16, device="cuda") for _ in range(n_layers)]
-    calls, keep, outs = [], [], []
-    for l, L in enumerate(layers):
+    calls, keep, outs, want = [], [], [], []
+    hb = h0
+    for l in range(n_layers):
+        # each layer's weights are made, packed and run through the oracle
+        # in turn, so that the host holds one layer at a time
+        L = synth.chained_layer(l)
+        r = oracle.chained_layer(L.w, L.ws, L.ws_num, L.gamma, L.attn_out, hb)
+        want.append(r)
+        hb = r["h2"]
         p = {k: bl.pack_ternary_weights(dev(v)) for k, v in L.w.items()}
         wsd = {k: bf16_dev(v) for k, v in L.ws.items()}
         gm = {k: bf16_dev(v) for k, v in L.gamma.items()}
@@ -175,12 +184,6 @@ def test_chained_two_layers_as_graph(bl):
     # from gate+up's epilogue
     assert graph.kernels == 3 * n_layers
     assert graph.linked == n_layers
-    # oracle chain
-    want, hb = [], h0
-    for L in layers:
-        r = oracle.chained_layer(L.w, L.ws, L.ws_num, L.gamma, L.attn_out, hb)
-        want.append(r)
-        hb = r["h2"]
     scratch = torch.randn(1 << 20, device="cuda")
     for rep in range(3):
         # every output poisoned, and unrelated eager work, between replays
