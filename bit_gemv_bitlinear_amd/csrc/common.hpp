@@ -175,7 +175,6 @@ constexpr int kDppQuadXor2 = 0x4E;   // quad_perm(2, 3, 0, 1)
 constexpr int kDppRowRor4 = 0x124;   // lane i <- lane (i + 4) % 16 inside each 16 lanes
 constexpr int kDppRowRor8 = 0x128;   // lane i <- lane (i + 8) % 16
 constexpr int kDppRowHalfMirror = 0x141;   // lane i <- lane 7 - i inside each 8 lanes
-constexpr int kDppRowBcast15 = 0x142;      // each lane of row r <- lane 15 of row r - 1 (r >= 1)
 
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, __int_as_float(dpp_row<kDppQuadXor1>(__float_as_int(v))));

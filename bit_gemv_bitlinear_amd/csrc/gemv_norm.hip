@@ -28,6 +28,8 @@ namespace {
 // all issued before the first wait.
 // ---------------------------------------------------------------------------
 
+constexpr int kDppRowBcast15 = 0x142;   // each lane of row r <- lane 15 of row r - 1 (r >= 1)
+
 // Sum of a double over the 64 lanes: the two 32-bit halves move together
 // through the DPP steps of wave_sum (pairs, quads, rotations by 4 and 8 inside
 // each row of 16), then the four row totals are read out and added.  The
