@@ -23,9 +23,13 @@ namespace {
 //   y = bf16(acc * ws / s), or bf16(residual + that) when a residual is given.
 // The glue runs in the prologue of every workgroup (the row is at most a few
 // thousand elements, read from L2 by each): no kernel of its own, so a chained
-// decode step launches one kernel per projection.  Everything else is the
-// staged GEMV of gemv.hip (its pieces in gemv_core.hpp): the weight loads are
-// all issued before the first wait.
+// decode step launches one kernel per projection.  In a graph, the MLP's
+// activation and the two statistics of down's RMSNorm (the sum of m^2 and the
+// largest |m * gamma|) are instead computed once, in the epilogue of the
+// gate+up kernel whose output they come from, and handed to down as a row and
+// per-workgroup partials (NormLink; MODE kNormLinked on the consumer's side).
+// Everything else is the staged GEMV of gemv.hip (its pieces in
+// gemv_core.hpp): the weight loads are all issued before the first wait.
 // ---------------------------------------------------------------------------
 
 constexpr int kDppRowBcast15 = 0x142;   // each lane of row r <- lane 15 of row r - 1 (r >= 1)
