@@ -169,8 +169,8 @@ struct alignas(16) NormPart {
 };
 constexpr int kNormMaxParts = 256;   // partials one consumer reads (4 per lane)
 struct NormLink {
-    // producer (m_out null: none); its workgroups each take half / 16 / (B / 2)
-    // gate bands and the up bands of the same rows
+    // producer (m_out null: none); each of its half / 16 / (B / 2)
+    // workgroups takes B / 2 gate bands and the up bands of the same rows
     uint16_t* m_out;
     const uint16_t* gamma_next;
     NormPart* part_out;
