@@ -34,6 +34,8 @@ namespace bl {
 
 namespace {
 
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
 constexpr int kBins = 256;    // bit positions p of the magnitude sum T = sum_p H[p] * 2^p
 constexpr int kLimbs = 12;    // 32-bit limbs of T (< 2^61 * 2^255 < 2^316)
 
@@ -74,24 +76,36 @@ __global__ __launch_bounds__(256) void absmean_hist_kernel(const uint4* __restri
         v[j] = w[min(base + static_cast<size_t>(j) * 256, n8 - 1)];
     __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
     // Four partial sums, each at most the total: exact under the same bound.
+    // The two magnitudes of a 32-bit word are handled as a pair of 16-bit
+    // lanes: |w| for both, clamped to the largest finite bf16 (the weights
+    // must be finite; this only keeps every sum finite), and the smallest
+    // nonzero and the largest magnitude tracked with packed minima and
+    // maxima -- the exponent bounds follow from them, since max(b >> 7, 1)
+    // grows with b.  (b - 1, wrapping, takes a zero out of the minimum.)
+    // The kernel went from 2321 to 1221 instructions; the ternariser (all
+    // four kernels, 13824 x 2560) from 46.7 to 44.0-44.2 us, same box.
     double part[4] = {0.0, 0.0, 0.0, 0.0};
-    uint32_t emin = 255, emax = 0;
+    us2 bmin1 = us2{0xFFFFu, 0xFFFFu};   // min of (b - 1) over the weights, per lane
+    us2 bmax = us2{0u, 0u};
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
         const bool live = base + static_cast<size_t>(j) * 256 < n8;
         const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            uint32_t b = (d[k >> 1] >> (16 * (k & 1))) & 0x7FFFu;
-            b = (live && b < 0x7F80u) ? b : 0u;   // non-finite weights (undefined results) are skipped
-            if (b != 0u) {
-                const uint32_t e = max(b >> 7, 1u);
-                emin = min(emin, e);
-                emax = max(emax, e);
-            }
-            part[k & 3] += static_cast<double>(__uint_as_float(b << 16));
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t a = live ? (d[k] & 0x7FFF7FFFu) : 0u;
+            const us2 b = __builtin_elementwise_min(__builtin_bit_cast(us2, a), us2{0x7F7Fu, 0x7F7Fu});
+            bmin1 = __builtin_elementwise_min(bmin1, static_cast<us2>(b - us2{1u, 1u}));
+            bmax = __builtin_elementwise_max(bmax, b);
+            const uint32_t bb = __builtin_bit_cast(uint32_t, b);
+            part[(2 * k) & 3] += static_cast<double>(__uint_as_float(bb << 16));
+            part[(2 * k + 1) & 3] += static_cast<double>(__uint_as_float(bb & 0xFFFF0000u));
         }
     }
+    const uint32_t bhi = max(static_cast<uint32_t>(bmax.x), static_cast<uint32_t>(bmax.y));
+    const uint32_t blo = min(static_cast<uint32_t>(bmin1.x), static_cast<uint32_t>(bmin1.y)) + 1u;
+    const uint32_t emin = bhi != 0 ? max(blo >> 7, 1u) : 255u;   // blo is then a nonzero magnitude
+    const uint32_t emax = bhi != 0 ? max(bhi >> 7, 1u) : 0u;
     const double sum = (part[0] + part[1]) + (part[2] + part[3]);
     if (emax != 0 && emax - emin <= 38) {
         // sum = mant * 2^(ef - 1075); in units of 2^-133: mant * 2^(ef - 942)
