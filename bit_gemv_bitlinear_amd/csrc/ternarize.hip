@@ -53,18 +53,24 @@ __global__ void zero_hist_kernel(unsigned long long* __restrict__ hist) {
 // a magnitude with exponent field E and fraction f is m * 2^(E' - 1) units,
 // E' = max(E, 1), m = f + 128 [E >= 1].
 //
-// Each thread adds its 128 magnitudes in fp64.  They are multiples of
-// 2^(E'min - 1) units below 128 * 2^(E'max + 7), so the fp64 sum is exact
-// when E'max - E'min <= 38 (the sum then needs at most 53 bits); the thread
-// adds its 53-bit mantissa, as three 18-bit pieces, into the bins of its bit
-// positions.  A thread whose magnitudes span more binades adds them one by
-// one (bin E' - 1).  Workgroup bins stay below 2^32 (256 threads * 2^18, or
-// 32 Ki magnitudes * 255).  With finite magnitudes a thread's sum is below
-// 2^135, i.e. 2^268 units, so its pieces land in bins 0 .. 252.
-constexpr int kPerThread = 16;                      // 16-byte chunks (8 bf16 each) per thread
-constexpr size_t kHistItems = 256 * kPerThread;     // chunks per workgroup
+// Each thread adds its n = 8 PER magnitudes (PER 16-byte chunks) in fp64.
+// Each is a multiple of 2^(E'min - 1) units below 2^(E'max + 7), so in units
+// of 2^(E'min - 1) the sum is below n * 2^(E'max - E'min + 8): the fp64 sum
+// is exact when E'max - E'min <= 53 - 8 - ceil(log2 n) (38 for n = 128, 37
+// for n = 192); the thread then adds its 53-bit mantissa, as three 18-bit
+// pieces, into the bins of its bit positions.  A thread whose magnitudes span
+// more binades adds them one by one (bin E' - 1).  Workgroup bins stay below
+// 2^32 (256 threads * 2^18, or 48 Ki magnitudes * 255).  With finite
+// magnitudes (below 2^128) a thread's sum is below 2^136, i.e. 2^269 units,
+// so its pieces land in bins 0 .. 253.
+constexpr int ceil_log2(int n) { return n <= 1 ? 0 : 1 + ceil_log2((n + 1) / 2); }
+template <int PER>
 __global__ __launch_bounds__(256) void absmean_hist_kernel(const uint4* __restrict__ w, size_t n8,
                                                            unsigned long long* __restrict__ hist) {
+    constexpr int kPerThread = PER;
+    constexpr size_t kHistItems = 256 * kPerThread;     // chunks per workgroup
+    constexpr uint32_t kExactSpan = 53 - 8 - ceil_log2(8 * PER);
+    static_assert(kExactSpan >= 1 && 256ull * 8 * PER * 255 < (1ull << 32), "bins and spans");
     __shared__ uint32_t h[kBins];
     h[threadIdx.x] = 0;
     __syncthreads();
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(256) void absmean_hist_kernel(const uint4* __restri
     const uint32_t emin = bhi != 0 ? max(blo >> 7, 1u) : 255u;   // blo is then a nonzero magnitude
     const uint32_t emax = bhi != 0 ? max(bhi >> 7, 1u) : 0u;
     const double sum = (part[0] + part[1]) + (part[2] + part[3]);
-    if (emax != 0 && emax - emin <= 38) {
+    if (emax != 0 && emax - emin <= kExactSpan) {
         // sum = mant * 2^(ef - 1075); in units of 2^-133: mant * 2^(ef - 942)
         const unsigned long long bits = static_cast<unsigned long long>(__double_as_longlong(sum));
         unsigned long long mant = (bits & 0xFFFFFFFFFFFFFull) | (1ull << 52);
@@ -309,9 +315,20 @@ hipError_t launch_ternarize(const uint16_t* w, uint8_t* packed, uint16_t* scales
     const size_t count = static_cast<size_t>(N) * K;
     const size_t n8 = count / 8;   // K % 16 == 0
     zero_hist_kernel<<<1, kBins, 0, stream>>>(hist);
-    const unsigned hist_groups = static_cast<unsigned>((n8 + kHistItems - 1) / kHistItems);
-    absmean_hist_kernel<<<hist_groups, 256, 0, stream>>>(reinterpret_cast<const uint4*>(w), n8,
-                                                         hist);
+    // 24 chunks per thread for large matrices (fewer workgroups, so fewer of
+    // their bin additions contend on the same global bins: 13824 x 2560 44.2
+    // -> 40.4 us, same box; 28, 32 and 40 chunks 41.7 / 41.5 / 45.3 us), 16
+    // otherwise, so that small matrices still spread over the CUs.
+    const uint4* w4 = reinterpret_cast<const uint4*>(w);
+    constexpr size_t kLarge = 24 * 256;
+    if (n8 >= kLarge * 512) {
+        absmean_hist_kernel<24><<<static_cast<unsigned>((n8 + kLarge - 1) / kLarge), 256, 0, stream>>>(
+            w4, n8, hist);
+    } else {
+        constexpr size_t kSmall = 16 * 256;
+        absmean_hist_kernel<16><<<static_cast<unsigned>((n8 + kSmall - 1) / kSmall), 256, 0, stream>>>(
+            w4, n8, hist);
+    }
     absmean_finalize_kernel<<<1, 256, 0, stream>>>(hist, count, scales);
     const int S = (K + kTileK - 1) / kTileK;
     const size_t n_words = packed_bytes(N, K) / 4;

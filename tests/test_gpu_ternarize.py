@@ -56,14 +56,19 @@ def test_zero_matrix_and_tiny_weights(bl):
     check(bl, "tiny", tiny)
 
 
-def test_wide_range_subnormals_and_outlier(bl):
-    g = synth.rng(43)
-    N, K = 96, 512
+@pytest.mark.parametrize("N,K", [(96, 512), (13824, 2560)])
+def test_wide_range_subnormals_and_outlier(bl, N, K):
+    # magnitudes over 170 binades: most threads' spans exceed the fp64 fast
+    # path's bound and take the per-weight bins, some do not; at 13824 x 2560
+    # the mean pass runs 24 chunks per thread (a bound of 37 binades), at 96 x
+    # 512 16 (38)
+    g = synth.rng(43 + N % 7)
     e = g.integers(-140, 30, size=(N, K)).astype(np.float64)
     v = (g.standard_normal((N, K)) * np.exp2(e)).astype(np.float32)
     check(bl, "wide range", (v.view(np.uint32) >> 16).astype(np.uint16))
     w = synth.weights_bf16(g, N, K)
     w[5, 7] = np.array([1e30], dtype=np.float32).view(np.uint32)[0] >> 16   # ~1e30 in bf16
+    w[N - 1, K - 1] = np.array([3e-40], dtype=np.float32).view(np.uint32)[0] >> 16   # subnormal
     check(bl, "outlier", w)
 
 
