@@ -37,8 +37,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ w,
                                                    int32_t* __restrict__ n_invalid) {
     const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= n_words) return;
-    const size_t t = i >> 8;
-    const int u = static_cast<int>(i & 255);
+    const size_t t = blockIdx.x;   // 256 threads per workgroup: the tile is i >> 8
+    const int u = static_cast<int>(threadIdx.x);
     const int q = u >> 2;
     const int n = static_cast<int>(t / S) * kTileRows + 4 * (q >> 4) + (u & 3);
     const int k0 = static_cast<int>(t % S) * kTileK + 16 * (q & 15);
@@ -49,12 +49,26 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ w,
         if (VEC) {
             const uint4 v = *reinterpret_cast<const uint4*>(row + k0);
             const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+            // Four weights at a time: element 4j + b is byte b of d[j] and
+            // goes to bits 8b + 2j; for w in {-1, 0, 1} its code w + 2 is
+            // (w & 3) ^ 2.  A byte outside {-1, 0, 1} is counted by a byte-
+            // parallel test: its low seven bits, flipped when negative, must be
+            // 0 (negative: -1) or at most 1 (positive); a nonzero remainder
+            // sets bit 7 when 0x7F is added (no carries: every byte <= 0x7F).
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int wv = static_cast<int8_t>((d[e >> 2] >> (8 * (e & 3))) & 0xFF);
-                const uint32_t c = ternary_code(wv);
-                bad += (c == 0);
-                word |= c << bit_of(e);
+            for (int j = 0; j < 4; ++j) {
+                word |= ((d[j] & 0x03030303u) ^ 0x02020202u) << (2 * j);
+                const uint32_t neg = (d[j] & 0x80808080u) >> 7;
+                const uint32_t rest = ((d[j] & 0x7F7F7F7Fu) ^ (neg * 0x7Fu)) & (0x7E7E7E7Eu | neg);
+                bad += __popc((rest + 0x7F7F7F7Fu) & 0x80808080u);
+            }
+            if (bad) {   // rare: the per-weight codes, 0 for such a weight, as the host twin makes them
+                word = 0;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int wv = static_cast<int8_t>((d[e >> 2] >> (8 * (e & 3))) & 0xFF);
+                    word |= ternary_code(wv) << bit_of(e);
+                }
             }
         } else {
             for (int e = 0; e < 16; ++e) {

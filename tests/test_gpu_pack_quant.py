@@ -59,6 +59,27 @@ def test_pack_unaligned_source_and_invalid_count(bl):
     np.testing.assert_array_equal(packed.cpu().numpy(), host)
 
 
+def test_pack_aligned_source_invalid_values(bl):
+    # the 16-byte path: codes four weights at a time and a byte-parallel count
+    # of the weights outside {-1, 0, 1}; rows 3 and 40 hold every int8 value
+    # once (253 invalid each), and a word with one invalid weight among valid
+    # ones, all checked against the host twin byte for byte
+    import torch
+    print("pack aligned source, invalid values", flush=True)
+    N, K = 64, 256
+    w = synth.ternary_uniform(synth.rng(6), N, K)
+    w[3] = np.arange(-128, 128, dtype=np.int8)
+    w[40] = np.arange(127, -129, -1).astype(np.int8)
+    w[10, 17] = 2
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    packed = bl.pack_ternary_weights(dev(w), n_invalid=bad)
+    torch.cuda.synchronize()
+    host, nbad = bl.bl_pack_ternary_host(w)
+    assert nbad == 2 * 253 + 1
+    assert int(bad.item()) == nbad
+    np.testing.assert_array_equal(packed.cpu().numpy(), host)
+
+
 def _quant_cases():
     g = synth.rng(99)
     cases = []
