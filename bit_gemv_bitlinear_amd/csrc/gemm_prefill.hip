@@ -50,16 +50,19 @@ constexpr int kRawBufferFlags = 0x00020000;   // word 3 of a buffer descriptor: 
 constexpr int kAPitch = 272;
 constexpr int kWRowGroupWords = 72;
 constexpr int kWTileWords = 4 * kWRowGroupWords;
-// The unsigned codes c = w + 2 of one packed word as the MFMA's A operand,
-// K order restored by shifting each 2-bit field down (padding stays 0): the
-// MFMA then sums c * x, and the epilogue takes 2 * sum(x) off each row.
-__device__ __forceinline__ v4i decode_w(uint32_t w) {
-    v4i b;
-    b.x = static_cast<int>(w & 0x03030303u);
-    b.y = static_cast<int>((w >> 2) & 0x03030303u);
-    b.z = static_cast<int>((w >> 4) & 0x03030303u);
-    b.w = static_cast<int>((w >> 6) & 0x03030303u);
-    return b;
+// The unsigned codes c = w + 2 of two packed words as two A operands of the
+// MFMA, K order restored by shifting each 2-bit field down (padding stays 0):
+// the MFMA then sums c * x, and the epilogue takes 2 * sum(x) off each row.
+// One 64-bit shift serves both words (the bits it moves from one word into
+// the other fall outside the mask): 11 VALU for two words instead of 14.
+// Same box, 13824 x 2560: M = 256 15.78 -> 15.47 us, M = 512 24.37 -> 24.22.
+__device__ __forceinline__ void decode_w2(uint32_t w0, uint32_t w1, v4i& a, v4i& b) {
+    const uint64_t p = (static_cast<uint64_t>(w1) << 32) | w0;
+    constexpr uint64_t m = 0x0303030303030303ull;
+    const uint64_t f0 = p & m, f1 = (p >> 2) & m, f2 = (p >> 4) & m, f3 = (p >> 6) & m;
+    a = v4i{static_cast<int>(f0), static_cast<int>(f1), static_cast<int>(f2), static_cast<int>(f3)};
+    b = v4i{static_cast<int>(f0 >> 32), static_cast<int>(f1 >> 32), static_cast<int>(f2 >> 32),
+            static_cast<int>(f3 >> 32)};
 }
 
 // WN x WMW wavefronts; wavefront tile 64 weight rows x 16 * MTW activation rows.
@@ -200,8 +203,9 @@ __global__ __launch_bounds__(WN * WMW * 64) void gemm_prefill_kernel(
         for (int st = 0; st < 4; ++st) {
             v4i wa[4];
 #pragma unroll
-            for (int tw = 0; tw < 4; ++tw)
-                wa[tw] = decode_w(w_lds[buf][w_rd + tw * kWTileWords + 16 * st]);
+            for (int tw = 0; tw < 4; tw += 2)
+                decode_w2(w_lds[buf][w_rd + tw * kWTileWords + 16 * st],
+                          w_lds[buf][w_rd + (tw + 1) * kWTileWords + 16 * st], wa[tw], wa[tw + 1]);
             v4i xb[MTW];
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt)
