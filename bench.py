@@ -26,7 +26,7 @@ Method (the same for every launch-per-step workload):
   * bytes per GEMV = N*K/4 (packed weights) + M*K (int8 x) + 2*M*N (bf16 y)
     + 4*M (s) + 2*ws_num (ws) -- the algorithmic bytes, each read once.
 
-Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+Prints one JSON line.  ``--gpus`` above 1 is refused: the layer runs on one GPU.
 """
 import argparse
 import hashlib
@@ -639,7 +639,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer is not sharded across GPUs in this build)", file=sys.stderr)
+              "(the layer runs on one GPU and is not sharded across GPUs)", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1:
         print("--steps must be at least 1", file=sys.stderr)
