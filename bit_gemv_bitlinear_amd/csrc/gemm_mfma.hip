@@ -57,6 +57,22 @@ __device__ __forceinline__ v4i decode_b(uint32_t w) {
     return b;
 }
 
+// Two words at once: one 64-bit shift per field serves both (what it moves
+// from one word into the other falls outside the mask), 19 VALU for two
+// words instead of 22.  Used with one m tile only: same box, M = 16 on
+// 2560 x 6912 and 13824 x 5120 9.16 / 7.70 -> 9.09 / 7.61 us, but M = 64
+// (four m tiles) 17.93 / 15.77 -> 18.15 / 15.83 us.
+__device__ __forceinline__ void decode_b2(uint32_t w0, uint32_t w1, v4i& a, v4i& b) {
+    const uint64_t p = (static_cast<uint64_t>(w1) << 32) | w0;
+    constexpr uint64_t m = 0x0303030303030303ull;
+    const uint64_t f0 = p & m, f1 = (p >> 2) & m, f2 = (p >> 4) & m, f3 = (p >> 6) & m;
+    auto cv = [](uint64_t f) {
+        return static_cast<int>(__builtin_amdgcn_perm(0u, kCodeToInt8, static_cast<uint32_t>(f)));
+    };
+    a = v4i{cv(f0), cv(f1), cv(f2), cv(f3)};
+    b = v4i{cv(f0 >> 32), cv(f1 >> 32), cv(f2 >> 32), cv(f3 >> 32)};
+}
+
 // A operands of one 64-K step for MT m tiles, as loaded: 16 bytes of each m
 // tile's row (this lane's row) at K offset 64*st + 16*chunk, from clamped
 // addresses so that the loads are unconditional.
@@ -186,12 +202,22 @@ __global__ __launch_bounds__(kMfmaMaxWaves * 64) void gemm_mfma_kernel(
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if constexpr (MT == 1) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const v4i b = decode_b(bw[p][t]);
+                for (int t = 0; t < 4; t += 2) {
+                    v4i b0, b1;
+                    decode_b2(bw[p][t], bw[p][t + 1], b0, b1);
+                    c[0][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[0], b0, c[0][t], 0, 0, 0);
+                    c[0][t + 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[0], b1, c[0][t + 1], 0, 0, 0);
+                }
+            } else {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    c[mt][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[mt], b, c[mt][t], 0, 0, 0);
+                for (int t = 0; t < 4; ++t) {
+                    const v4i b = decode_b(bw[p][t]);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        c[mt][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap[mt], b, c[mt][t], 0, 0, 0);
+                }
             }
         }
     }

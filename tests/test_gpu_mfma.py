@@ -52,8 +52,12 @@ def test_batched_model_shape(bl, M):
 
 @pytest.mark.parametrize("M,N,K", [(2, 64, 64), (15, 100, 208), (16, 64 * 3, 2560), (17, 130, 80),
                                    (33, 640, 6912), (64, 256, 1024), (65, 192, 144),
-                                   (130, 70, 272), (64, 2560, 13824)])
+                                   (130, 70, 272), (64, 2560, 13824),
+                                   (2, 2560, 6912), (16, 2560, 6912), (7, 130, 2576), (12, 4000, 5120)])
 def test_shapes(bl, M, N, K):
+    # M <= 16 with K > 2560 (the last four) runs the streaming kernel with one
+    # m tile: the down projection of a decode batch, K just past the band
+    # kernel's range with N ragged, and a K = 5120 layer
     c = synth.make_int8_gemv(f"m{M}", M, N, K, 1, synth.seed_for(8, 0, M + N % 89))
     check(bl, c.name, c.w, c.xq, c.s, c.ws, c.ws_num)
 
